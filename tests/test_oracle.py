@@ -1,0 +1,329 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a
+closed form printed on the pages, a worked example, a library routine
+that the definition reduces to in a special case, an invariance of
+softmax attention, or finite differences.  A plausible slip anywhere in
+the oracle (a wrong comparison in the mask, a dropped scale, natural vs
+base-2 logarithm, a transposed operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, mask=None, is_causal=False, scale=None):
+    """torch's scaled_dot_product_attention on one head in float64."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, is_causal=is_causal, scale=scale)
+    return o[0, 0].numpy()
+
+
+def _blocks(n, b):
+    """Consecutive runs of b positions from the start of a half."""
+    return [list(range(s, min(s + b, n))) for s in range(0, n, b)]
+
+
+# --------------------------------------------------------------------------
+# Mask: cardinality (closed form on page 1) and brute force on tiny sizes
+# --------------------------------------------------------------------------
+
+def test_visible_pairs_closed_form_all_workloads():
+    """Fast Diffusion Attention, 'The right yardstick': n^2 + n*b pairs."""
+    with open(os.path.join(GOLDEN, "visible_pairs.json")) as f:
+        gold = json.load(f)["workloads"]
+    seen = set()
+    for name, w in WORKLOADS.items():
+        key = (w.n, w.b)
+        if key in seen:
+            continue
+        seen.add(key)
+        total = 0
+        for r0 in range(0, 2 * w.n, 2048):  # row chunks keep memory small
+            total += int(oracle.block_diffusion_mask(w.n, w.b, np.arange(r0, min(r0 + 2048, 2 * w.n))).sum())
+        assert total == gold[name]["pairs"], name
+        if w.n % w.b == 0:
+            assert total == w.n * w.n + w.n * w.b
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 11])
+def test_mask_matches_block_description_bruteforce(n):
+    """Tiny sizes: the mask equals the prose of 'Block diffusion in one picture'
+    evaluated on explicit lists of blocks."""
+    for b in range(1, n + 3):
+        M = oracle.block_diffusion_mask(n, b)
+        blocks = _blocks(n, b)
+        want = np.zeros((2 * n, 2 * n), dtype=bool)
+        for i, blk in enumerate(blocks):
+            for r in blk:
+                # noisy row: its own noisy block, both directions
+                for c in blk:
+                    want[r, c] = True
+                # noisy row: every clean block strictly before block i
+                for earlier in blocks[:i]:
+                    for c in earlier:
+                        want[r, n + c] = True
+                # clean row: its own clean block and the earlier clean blocks
+                for earlier in blocks[: i + 1]:
+                    for c in earlier:
+                        want[n + r, n + c] = True
+        assert np.array_equal(M, want), (n, b)
+        # staircase equivalence ('The right yardstick'): noisy row block i sees
+        # i blocks in total, like a causal row over blocks
+        for i, blk in enumerate(blocks):
+            r = blk[0]
+            assert M[r, n:].sum() == sum(len(x) for x in blocks[:i])
+
+
+def test_causal_mask_is_lower_triangular():
+    for S in (1, 2, 7, 33):
+        assert np.array_equal(oracle.causal_mask(S), np.tril(np.ones((S, S), dtype=bool)))
+
+
+# --------------------------------------------------------------------------
+# Forward: sub-problems that reduce to textbook attention
+# --------------------------------------------------------------------------
+
+CASES = [(16, 4, 8), (13, 3, 8), (20, 1, 4), (9, 9, 6), (12, 20, 5), (32, 8, 16)]
+
+
+@pytest.mark.parametrize("n,b,D", CASES)
+def test_clean_half_is_block_causal_attention(n, b, D):
+    """The clean half sees only clean keys, block-causally ('Block diffusion in
+    one picture'); compare with SDPA over the clean tokens alone and an
+    independently built block-causal mask (Kronecker product)."""
+    q, k, v = (_rand((2 * n, D), s) for s in (1, 2, 3))
+    scale = 1 / math.sqrt(D)
+    O, lse = oracle.diffusion_forward(q, k, v, b, scale)
+    nb = -(-n // b)
+    bc = np.kron(np.tril(np.ones((nb, nb))), np.ones((b, b)))[:n, :n].astype(bool)
+    want = _sdpa(q[n:], k[n:], v[n:], mask=bc, scale=scale)
+    np.testing.assert_allclose(O[n:], want, rtol=0, atol=1e-12)
+    # log-sum-exp of the clean rows, natural log, including the scale
+    S = scale * q[n:] @ k[n:].T
+    S = np.where(bc, S, -np.inf)
+    want_lse = np.log(np.exp(S).sum(axis=1))
+    np.testing.assert_allclose(lse[n:], want_lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,b,D", CASES)
+def test_noisy_block_attends_to_earlier_clean_plus_itself(n, b, D):
+    """Noisy block i = plain (unmasked) attention over
+    concat(clean blocks < i, noisy block i)."""
+    q, k, v = (_rand((2 * n, D), s) for s in (4, 5, 6))
+    scale = 0.37
+    O, lse = oracle.diffusion_forward(q, k, v, b, scale)
+    for i, blk in enumerate(_blocks(n, b)):
+        ctx = [n + c for c in range(0, blk[0])] + blk
+        want = _sdpa(q[blk], k[ctx], v[ctx], scale=scale)
+        np.testing.assert_allclose(O[blk], want, rtol=0, atol=1e-12)
+        S = scale * q[blk] @ k[ctx].T
+        np.testing.assert_allclose(lse[blk], np.log(np.exp(S).sum(axis=1)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,D", [(7, 4), (64, 16), (100, 8)])
+def test_block_size_one_clean_half_is_causal(n, D):
+    """With block size 1 the clean half is causal attention on the clean tokens
+    ('Accuracy' on page 1); torch's is_causal path in float64."""
+    q, k, v = (_rand((2 * n, D), s) for s in (7, 8, 9))
+    scale = 1 / math.sqrt(D)
+    O, _ = oracle.diffusion_forward(q, k, v, 1, scale)
+    want = _sdpa(q[n:], k[n:], v[n:], is_causal=True, scale=scale)
+    np.testing.assert_allclose(O[n:], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,b", [(5, 5), (6, 9), (10, 64)])
+def test_block_longer_than_half_is_bidirectional_per_half(n, b):
+    """b >= n: one block per half.  The noisy half has no earlier clean block,
+    so each half is full bidirectional attention over itself."""
+    D = 4
+    q, k, v = (_rand((2 * n, D), s) for s in (10, 11, 12))
+    O, _ = oracle.diffusion_forward(q, k, v, b, 0.5)
+    np.testing.assert_allclose(O[:n], _sdpa(q[:n], k[:n], v[:n], scale=0.5), atol=1e-12)
+    np.testing.assert_allclose(O[n:], _sdpa(q[n:], k[n:], v[n:], scale=0.5), atol=1e-12)
+
+
+@pytest.mark.parametrize("n,b", [(12, 4), (13, 5), (8, 1), (6, 8)])
+def test_zero_queries_closed_form(n, b):
+    """q = 0: every visible score is 0, so each row averages its visible values
+    and LSE_i = ln(number of visible keys)."""
+    D = 6
+    q = np.zeros((2 * n, D))
+    k, v = _rand((2 * n, D), 13), _rand((2 * n, D), 14)
+    O, lse = oracle.diffusion_forward(q, k, v, b, 1.0)
+    for i, blk in enumerate(_blocks(n, b)):
+        noisy_ctx = [n + c for c in range(blk[0])] + blk
+        clean_ctx = [n + c for c in range(blk[-1] + 1)]
+        for r in blk:
+            np.testing.assert_allclose(O[r], v[noisy_ctx].mean(axis=0), atol=1e-13)
+            assert abs(lse[r] - math.log(len(noisy_ctx))) < 1e-13
+            np.testing.assert_allclose(O[n + r], v[clean_ctx].mean(axis=0), atol=1e-13)
+            assert abs(lse[n + r] - math.log(len(clean_ctx))) < 1e-13
+
+
+def test_shift_invariances():
+    """Adding c to every key leaves O unchanged and shifts LSE_i by
+    scale*q_i.c; adding c to every value shifts O by c."""
+    n, b, D, scale = 10, 3, 5, 0.7
+    q, k, v = (_rand((2 * n, D), s) for s in (15, 16, 17))
+    c = _rand((D,), 18)
+    O, lse = oracle.diffusion_forward(q, k, v, b, scale)
+    O2, lse2 = oracle.diffusion_forward(q, k + c, v, b, scale)
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + scale * q @ c, atol=1e-12)
+    O3, lse3 = oracle.diffusion_forward(q, k, v + c, b, scale)
+    np.testing.assert_allclose(O3, O + c, atol=1e-12)
+    np.testing.assert_allclose(lse3, lse, atol=1e-13)
+
+
+def test_worked_example_of_online_softmax():
+    """FlashAttention page, section 4.3: the row [1, 2 | 0, 3] in two blocks.
+    (a) the oracle's softmax of the four scores equals the page's final
+    weights; (b) the page's block-by-block recurrence (running max m,
+    rescale e^(m - m'), new block weights) reproduces the same weights."""
+    with open(os.path.join(GOLDEN, "online_softmax_worked_example.json")) as f:
+        g = json.load(f)
+    w = np.exp(np.array(g["final_weight_exponents"]))
+    want = w / w.sum()
+    # (a) one noisy row (n = 4, b = 4: the row sees the 4 noisy keys and
+    # nothing else); q . k_j = score_j with scale 1; one-hot values read P.
+    n, D = 4, 8
+    q = np.zeros((2 * n, D))
+    k = np.zeros((2 * n, D))
+    q[0, 0] = 1.0
+    k[:n, 0] = g["scores"]
+    v = np.eye(2 * n, D)
+    O, lse = oracle.diffusion_forward(q, k, v, 4, 1.0)
+    np.testing.assert_allclose(O[0, :n], want, atol=1e-15)
+    assert abs(lse[0] - (max(g["scores"]) + math.log(w.sum()))) < 1e-14
+    # (b) the recurrence as the page states it, with its printed intermediates
+    b1, b2 = (np.array(x) for x in g["blocks"])
+    m = b1.max()
+    assert m == g["block1_max"]
+    np.testing.assert_allclose(b1 - m, g["block1_weight_exponents"])
+    m2 = max(m, b2.max())
+    assert m2 == g["block2_max"] and m - m2 == g["rescale_exponent"]
+    np.testing.assert_allclose(b1 - m + (m - m2), g["block1_rescaled_exponents"])
+    np.testing.assert_allclose(b2 - m2, g["block2_weight_exponents"])
+    ell = np.exp(b1 - m).sum() * math.exp(m - m2) + np.exp(b2 - m2).sum()
+    np.testing.assert_allclose(np.concatenate([np.exp(b1 - m2), np.exp(b2 - m2)]) / ell, want, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Backward: finite differences and gradient identities
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,b", [(4, 1), (5, 2), (6, 3), (3, 4), (8, 2)])
+def test_gradients_match_central_differences(n, b):
+    """Central differences of L = sum(dout * O) in float64; rel. error <= 1e-6."""
+    D, scale, eps = 4, 0.8, 1e-6
+    q, k, v, do = (_rand((2 * n, D), s) for s in (19, 20, 21, 22))
+    dq, dk, dv = oracle.diffusion_backward(q, k, v, do, b, scale)
+
+    def loss(qq, kk, vv):
+        return float((oracle.diffusion_forward(qq, kk, vv, b, scale)[0] * do).sum())
+
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        err = np.abs(num - grad).max() / np.abs(grad).max()
+        assert err <= 1e-6, (which, err)
+
+
+def test_gradient_identities():
+    """Shift invariance gives sum_j dK_j = 0 (every row of dS sums to zero) and
+    sum_j dV_j = sum_i dO_i (every row of P sums to one); the score scale
+    gives sum_i q_i.dQ_i = sum_j k_j.dK_j."""
+    n, b, D, scale = 14, 4, 6, 0.45
+    q, k, v, do = (_rand((2 * n, D), s) for s in (23, 24, 25, 26))
+    dq, dk, dv = oracle.diffusion_backward(q, k, v, do, b, scale)
+    np.testing.assert_allclose(dk.sum(axis=0), 0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+    assert abs((q * dq).sum() - (k * dk).sum()) < 1e-11
+    # delta computed two ways: sum_j P_ij dP_ij == dO_i . O_i
+    O, _ = oracle.diffusion_forward(q, k, v, b, scale)
+    M = oracle.block_diffusion_mask(n, b)
+    S = np.where(M, scale * q @ k.T, -np.inf)
+    P = np.exp(S - S.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    np.testing.assert_allclose((P * (do @ v.T)).sum(1), (do * O).sum(1), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# The causal yardstick and the sampled (row / column) forms
+# --------------------------------------------------------------------------
+
+def test_causal_oracle_matches_sdpa_and_finite_differences():
+    S, D = 11, 4
+    q, k, v, do = (_rand((S, D), s) for s in (27, 28, 29, 30))
+    O, lse = oracle.causal_forward(q, k, v, 0.6)
+    np.testing.assert_allclose(O, _sdpa(q, k, v, is_causal=True, scale=0.6), atol=1e-12)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    o = F.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=True, scale=0.6)[0]
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = oracle.causal_backward(q, k, v, do, 0.6)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("n,b", [(24, 5), (16, 16), (20, 1)])
+def test_sampled_forms_equal_full(n, b):
+    D, scale = 8, 0.3
+    q, k, v, do = (_rand((2 * n, D), s) for s in (31, 32, 33, 34))
+    O, lse = oracle.diffusion_forward(q, k, v, b, scale)
+    dq, dk, dv = oracle.diffusion_backward(q, k, v, do, b, scale)
+    rows = [0, 3, n - 1, n, n + 7, 2 * n - 1]
+    Or, lr = oracle.diffusion_forward_rows(q, k, v, b, scale, rows)
+    np.testing.assert_allclose(Or, O[rows], atol=1e-13)
+    np.testing.assert_allclose(lr, lse[rows], atol=1e-13)
+    np.testing.assert_allclose(oracle.diffusion_grad_q_rows(q, k, v, do, b, scale, rows), dq[rows], atol=1e-12)
+    cols = [0, 1, n - 2, n, n + 3, 2 * n - 1]
+    dkc, dvc = oracle.diffusion_grad_kv_cols(q, k, v, do, O, lse, b, scale, cols)
+    np.testing.assert_allclose(dkc, dk[cols], atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
+
+
+def test_batched_layout_against_sdpa():
+    """(batch, 2n, heads, dim) handling: at block size 1 the clean half of every
+    (sample, head) equals causal SDPA run in torch's (B, H, S, D) layout."""
+    B, n, H, D = 2, 9, 3, 4
+    q, k, v, _ = make_inputs(B, n, H, D, seed=7)
+    O, lse = oracle.batched(oracle.diffusion_forward, oracle.to_f64(q), oracle.to_f64(k),
+                            oracle.to_f64(v), b=1, scale=0.5)
+    assert O.shape == (B, 2 * n, H, D) and lse.shape == (B, H, 2 * n)
+    t = lambda x: x.to(torch.float64)[:, n:].permute(0, 2, 1, 3)
+    want = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True, scale=0.5)
+    np.testing.assert_allclose(O[:, n:], want.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+def test_inputs_are_seeded_bf16():
+    a = make_inputs(1, 8, 2, 4, seed=3)
+    b = make_inputs(1, 8, 2, 4, seed=3)
+    for x, y in zip(a, b):
+        assert x.dtype == torch.bfloat16 and x.shape == (1, 16, 2, 4)
+        assert torch.equal(x, y)
+    c = make_inputs(1, 8, 2, 4, seed=4)
+    assert not torch.equal(a[0], c[0])

@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs for block-diffusion attention.
+
+This module is shared by the CPU oracle, the tests and the benchmark.  It
+holds shapes, seeds and random draws only -- none of the attention
+arithmetic -- so that the oracle and the HIP path see identical bits
+without sharing any code that computes the method.
+
+Layout (Fast Diffusion Attention, "TL;DR" usage line): q, k, v and the
+output gradient have shape (batch, 2n, heads, headdim); along dim 1 the
+first n tokens are the noisy half and the last n the clean half.
+
+Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws
+float32 N(0, 1) values in the order q, k, v, dout; each is rounded to
+bfloat16 (round-to-nearest-even, torch's ``.to``).  The pages benchmark on
+FlashAttention's benchmark shapes, which they do not list; the synthetic
+workloads below stand in for them.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Tuple
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One problem: B samples of 2n tokens, H heads of width D, block size b."""
+
+    name: str
+    B: int
+    n: int
+    H: int
+    D: int
+    b: int
+    seed: int
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, 2 * self.n, self.H, self.D)
+
+    def describe(self) -> str:
+        return (f"{self.name}: B={self.B} n={self.n} (2n={2 * self.n}) H={self.H} "
+                f"D={self.D} b={self.b} seed={self.seed}")
+
+
+def _c5(D: int, b: int) -> Workload:
+    return Workload(f"c5_d{D}_b{b}", B=4, n=4096, H=16, D=D, b=b, seed=1005 if D == 64 else 1006)
+
+
+# The five workloads of the block-diffusion attention study: a tiny case, a
+# short-sequence case, a medium case with the causal yardstick, the
+# long-sequence case (the largest, on which throughput is quoted) and a
+# block-size sweep with tile-misaligned and tile-sized blocks.
+WORKLOADS: Dict[str, Workload] = {
+    "c1": Workload("c1", B=1, n=128, H=2, D=64, b=4, seed=1001),
+    "c2": Workload("c2", B=4, n=1024, H=16, D=64, b=4, seed=1002),
+    "c3": Workload("c3", B=8, n=2048, H=16, D=128, b=16, seed=1003),
+    "c4": Workload("c4", B=2, n=8192, H=32, D=128, b=32, seed=1004),
+}
+for _D in (64, 128):
+    for _b in (1, 3, 48, 128, 256):
+        _w = _c5(_D, _b)
+        WORKLOADS[_w.name] = _w
+
+LARGEST = "c4"
+
+
+def make_inputs(B: int, n: int, H: int, D: int, seed: int, with_dout: bool = True):
+    """Return bf16 CPU tensors (q, k, v, dout) of shape (B, 2n, H, D).
+
+    Draw order is fixed (q, k, v, dout) so that every consumer of a seed
+    sees the same bits.  ``with_dout=False`` still draws nothing extra and
+    returns dout as None.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (B, 2 * n, H, D)
+    out = []
+    for _ in range(4 if with_dout else 3):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        out.append(x.to(torch.bfloat16))
+    if not with_dout:
+        out.append(None)
+    return tuple(out)
+
+
+def make_workload_inputs(w: Workload, with_dout: bool = True):
+    return make_inputs(w.B, w.n, w.H, w.D, w.seed, with_dout=with_dout)
+
+
+def make_causal_view(x: torch.Tensor) -> torch.Tensor:
+    """View (B, 2n, H, D) as (2B, n, H, D): each half becomes one sequence.
+
+    This is a pure reshape (no arithmetic): the same bytes seen as 2B
+    sequences of length n, the equal-work causal problem.
+    """
+    B, twon, H, D = x.shape
+    return x.reshape(2 * B, twon // 2, H, D)
