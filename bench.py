@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of block-diffusion attention (forward + backward) on one MI355X.
+
+One step is the whole hot path on one batch: the forward kernel, then the
+three backward kernels (delta, dK/dV, dQ), all through the C ABI of
+libbdattn.so on torch's current stream, with inputs resident in HBM.
+
+Throughput counts visible (query, key) pairs only (Fast Diffusion
+Attention, "The right yardstick"): 4 * pairs * headdim * heads * batch flops
+for the forward pass and 2.5 times that for the backward pass.  The
+yardstick is the library's own causal kernel on the same bytes viewed as 2B
+sequences of n tokens, timed in interleaved rounds with the diffusion kernel
+in one process and reported as medians (the pages' protocol for clocks that
+follow power draw).
+
+Prints one JSON line.  Default workload: the long-sequence problem
+(B=2, n=8192, H=32, D=128, block size 32).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs(n: int, b: int) -> int:
+    """n^2 + sum of squared block sizes ("The right yardstick": n^2 + n*b)."""
+    full, rest = divmod(n, b)
+    return n * n + full * b * b + rest * rest
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--rounds", type=int, default=5, help="interleaved diffusion/causal rounds")
+    ap.add_argument("--round-ms", type=float, default=300.0, help="target duration of each phase of a round")
+    ap.add_argument("--no-causal", action="store_true", help="skip the causal yardstick rounds")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="query rows per half in the oracle's timed sample")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, do, rows_per_half):
+    """Time the float64 oracle (as it stands) on a bounded sample: a chunk of
+    query rows from each half of one (sample, head), forward and backward."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    n, scale = w.n, 1.0 / math.sqrt(w.D)
+    f = lambda x: oracle.to_f64(x[0, :, 0])
+    qh, kh, vh, dh = f(q), f(k), f(v), f(do)
+    r = min(rows_per_half, n)
+    mid = (n - r) // 2
+    rows = np.concatenate([np.arange(mid, mid + r), n + np.arange(mid, mid + r)])
+    M = oracle.block_diffusion_mask(n, w.b, rows)
+    pairs = int(M.sum())
+    t0 = time.perf_counter()
+    oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
+    t1 = time.perf_counter()
+    oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
+    t2 = time.perf_counter()
+    flops = 3.5 * 4 * pairs * w.D
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 oracle forward + backward of {2 * r} query rows ({r} per half) of one "
+                   f"(sample, head) of {w.name}, all {2 * n} keys; {pairs} visible pairs; "
+                   f"{t1 - t0:.2f} s forward, {t2 - t1:.2f} s backward; host {platform.processor() or platform.machine()}"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the attention of every (sample, head) is independent; see the design notes "
+              "for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_diffusion_lm_amd as bd
+    from workloads import WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, n, H, D, b = w.B, w.n, w.H, w.D, w.b
+    T = 2 * n
+    scale = 1.0 / math.sqrt(D)
+
+    q_c, k_c, v_c, do_c = make_workload_inputs(w)
+    q, k, v, do = (x.to(dev) for x in (q_c, k_c, v_c, do_c))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws_bytes = bd.diffusion_attn_bwd_workspace_size(B, n, H, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # causal yardstick: the same bytes as 2B sequences of n tokens
+    cq, ck, cv, cdo = (x.view(2 * B, n, H, D) for x in (q, k, v, do))
+    cout = torch.empty_like(cq)
+    clse = torch.empty((2 * B, H, n), dtype=torch.float32, device=dev)
+    cdq, cdk, cdv = (torch.empty_like(cq) for _ in range(3))
+    cws = torch.empty(bd.causal_attn_bwd_workspace_size(2 * B, n, H, D), dtype=torch.uint8, device=dev)
+
+    MD, MC = bd.MODE_DIFFUSION, bd.MODE_CAUSAL
+
+    def diffusion_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+        if ev is not None:
+            ev[1].record()
+        for stage in range(3):
+            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, b, scale, ws, ws_bytes)
+            if ev is not None:
+                ev[2 + stage].record()
+
+    def causal_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
+        if ev is not None:
+            ev[1].record()
+        for stage in range(3):
+            bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, 2 * B, n, H, D, 1,
+                                scale, cws)
+            if ev is not None:
+                ev[2 + stage].record()
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    # ---- warm-up, then exactly K timed steps --------------------------------
+    for _ in range(args.warmup):
+        diffusion_step()
+    torch.cuda.synchronize()
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        diffusion_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    def split(ev_list):
+        per = {"fwd": [], "bwd_preprocess": [], "bwd_dkdv": [], "bwd_dq": []}
+        for ev in ev_list:
+            per["fwd"].append(ev[0].elapsed_time(ev[1]))
+            per["bwd_preprocess"].append(ev[1].elapsed_time(ev[2]))
+            per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
+            per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
+        return per
+
+    kern = split(evs)
+    kern_avg = {key: sum(vals) / len(vals) for key, vals in kern.items()}
+
+    P = visible_pairs(n, b)
+    assert P == bd.bdattn_visible_pairs(MD, n, b)
+    F_fwd = 4.0 * P * D * H * B
+    F_bwd = 2.5 * F_fwd
+    value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
+    t_fwd = kern_avg["fwd"]
+    t_bwd = kern_avg["bwd_preprocess"] + kern_avg["bwd_dkdv"] + kern_avg["bwd_dq"]
+
+    # ---- the dominant kernel against its roofline ---------------------------
+    per_kernel_flops = {"fwd": 2 * 2.0 * P * D * H * B,        # S = QK^T, O = PV
+                        "bwd_dkdv": 4 * 2.0 * P * D * H * B,   # S, dP, dV, dK
+                        "bwd_dq": 3 * 2.0 * P * D * H * B}     # S, dP, dQ
+    dom = max(per_kernel_flops, key=lambda kname: kern_avg[kname])
+    achieved = per_kernel_flops[dom] / (kern_avg[dom] * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel") == dom and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
+                "algorithmic_flops_per_launch": per_kernel_flops[dom],
+                "avg_launch_ms": kern_avg[dom]}
+
+    # ---- interleaved rounds against the causal yardstick --------------------
+    ratio = None
+    medians = None
+    if not args.no_causal:
+        for _ in range(2):
+            causal_step()
+        torch.cuda.synchronize()
+        reps = max(1, int(math.ceil(args.round_ms / max(ms_per_step, 1e-3))))
+        rounds = {"diff": [], "causal": []}
+        for _ in range(args.rounds):
+            for name, fn in (("diff", diffusion_step), ("causal", causal_step)):
+                ev_list = [new_events() for _ in range(reps)]
+                for i in range(reps):
+                    fn(ev_list[i])
+                torch.cuda.synchronize()
+                per = split(ev_list)
+                f = sum(per["fwd"]) / reps
+                bwd = sum(per["bwd_preprocess"][i] + per["bwd_dkdv"][i] + per["bwd_dq"][i] for i in range(reps)) / reps
+                rounds[name].append((f, bwd))
+        med = {name: (statistics.median(x[0] for x in r), statistics.median(x[1] for x in r),
+                      statistics.median(x[0] + x[1] for x in r)) for name, r in rounds.items()}
+        Pc = n * (n + 1) // 2
+        Fc_fwd = 4.0 * Pc * D * H * (2 * B)
+        tf = lambda F, ms: F / (ms * 1e-3) / 1e12
+        medians = {
+            "diffusion_tflops": {"fwd": tf(F_fwd, med["diff"][0]), "bwd": tf(F_bwd, med["diff"][1]),
+                                 "step": tf(F_fwd + F_bwd, med["diff"][2])},
+            "causal_tflops": {"fwd": tf(Fc_fwd, med["causal"][0]), "bwd": tf(2.5 * Fc_fwd, med["causal"][1]),
+                              "step": tf(3.5 * Fc_fwd, med["causal"][2])},
+            "reps_per_phase": reps, "rounds": args.rounds,
+        }
+        ratio = {kname: medians["diffusion_tflops"][kname] / medians["causal_tflops"][kname]
+                 for kname in ("fwd", "bwd", "step")}
+
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_rows)
+
+    line = {
+        "metric": "fwd+bwd TFLOPS (visible pairs only) and ratio vs own causal kernel on 2B×n",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "global_batch": B, "seq_len": T, "block_size": b,
+                   "heads": H, "headdim": D, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fwd_tflops": F_fwd / (t_fwd * 1e-3) / 1e12,
+        "bwd_tflops": F_bwd / (t_bwd * 1e-3) / 1e12,
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "ratio_vs_causal": ratio,
+        "interleaved_medians": medians,
+        "kernel_avg_ms": kern_avg,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

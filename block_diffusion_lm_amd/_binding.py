@@ -1,0 +1,219 @@
+"""ctypes binding of libbdattn.so: the C-ABI entry points under the same names.
+
+Argument marshalling only: every function checks that its tensors live on
+the GPU with the dtype and shape the C ABI expects, passes their device
+pointers and the current HIP stream, and turns a non-zero status into an
+exception.  All computation happens in the library's HIP kernels.  There is
+no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdattn.so")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); mirrors include/bdattn.h
+SIGNATURES = {
+    "bdattn_status_string": (ctypes.c_char_p, [_i]),
+    "diffusion_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "diffusion_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "diffusion_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "causal_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
+    "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "bdattn_fwd_tiles": (_i, [_i, _i, _i, _i, _i, _i, _i, _i32p, _i]),
+    "bdattn_bwd_tiles": (_i, [_i, _i, _i, _i, _i, _i, _i, _i32p, _i]),
+    "bdattn_row_interval": (_i, [_i, _i, _i, _i, _i, _i, _i32p, _i32p]),
+    "bdattn_visible_pairs": (ctypes.c_int64, [_i, _i, _i]),
+}
+
+MODE_DIFFUSION, MODE_CAUSAL = 0, 1
+NOISY, CLEAN = 0, 1
+
+_lib = None
+
+
+class BdattnError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libbdattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BdattnError(f"{LIB_PATH} is missing: build it with `python -m block_diffusion_lm_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().bdattn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise BdattnError(f"{what} failed: {status_string(code)} (status {code})")
+
+
+def _stream_handle(t: torch.Tensor, stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _want(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, block_size, scale, stream=None):
+    shp = (B, 2 * n, H, D)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _want(t, name, torch.bfloat16, shp)
+    _want(lse, "lse", torch.float32, (B, H, 2 * n))
+    _check(lib().diffusion_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, n, H, D,
+                                    block_size, float(scale), _stream_handle(q, stream)),
+           "diffusion_attn_fwd")
+
+
+def diffusion_attn_bwd_workspace_size(B, n, H, D) -> int:
+    return int(lib().diffusion_attn_bwd_workspace_size(B, n, H, D))
+
+
+def diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size, scale,
+                       workspace, workspace_bytes=None, stream=None):
+    shp = (B, 2 * n, H, D)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, torch.bfloat16, shp)
+    _want(lse, "lse", torch.float32, (B, H, 2 * n))
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    _check(lib().diffusion_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, D, block_size,
+                                    float(scale), _ptr(workspace), int(workspace_bytes),
+                                    _stream_handle(q, stream)),
+           "diffusion_attn_bwd")
+
+
+def causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale, stream=None):
+    shp = (B, S, H, D)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _want(t, name, torch.bfloat16, shp)
+    _want(lse, "lse", torch.float32, (B, H, S))
+    _check(lib().causal_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, D,
+                                 float(scale), _stream_handle(q, stream)),
+           "causal_attn_fwd")
+
+
+def causal_attn_bwd_workspace_size(B, S, H, D) -> int:
+    return int(lib().causal_attn_bwd_workspace_size(B, S, H, D))
+
+
+def causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, scale, workspace,
+                    workspace_bytes=None, stream=None):
+    shp = (B, S, H, D)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, torch.bfloat16, shp)
+    _want(lse, "lse", torch.float32, (B, H, S))
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    _check(lib().causal_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, S, H, D, float(scale),
+                                 _ptr(workspace), int(workspace_bytes), _stream_handle(q, stream)),
+           "causal_attn_bwd")
+
+
+def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size,
+                     scale, workspace, workspace_bytes=None, stream=None):
+    """One backward kernel (0: delta, 1: dK/dV, 2: dQ); n is S in causal mode."""
+    T = 2 * n if mode == MODE_DIFFUSION else n
+    shp = (B, T, H, D)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, torch.bfloat16, shp)
+    _want(lse, "lse", torch.float32, (B, H, T))
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda":
+        raise ValueError("workspace must be on the GPU")
+    _check(lib().bdattn_bwd_stage(mode, stage, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, D, block_size,
+                                  float(scale), _ptr(workspace), int(workspace_bytes),
+                                  _stream_handle(q, stream)),
+           "bdattn_bwd_stage")
+
+
+# ---------------------------------------------------------------------------
+# Host-side geometry inspection (no GPU needed)
+# ---------------------------------------------------------------------------
+
+def _tiles(fn, mode, n, block_size, tile_m, tile_n, half, tile):
+    cnt = fn(mode, n, block_size, tile_m, tile_n, half, tile, None, 0)
+    if cnt < 0:
+        raise ValueError("bad geometry arguments")
+    buf = (ctypes.c_int32 * max(1, 3 * cnt))()
+    fn(mode, n, block_size, tile_m, tile_n, half, tile, buf, cnt)
+    return [(buf[3 * i], buf[3 * i + 1], buf[3 * i + 2]) for i in range(cnt)]
+
+
+def bdattn_fwd_tiles(mode, n, block_size, tile_m, tile_n, qhalf, qt):
+    """[(key_half, key_tile, masked)] visited by query tile qt of half qhalf."""
+    return _tiles(lib().bdattn_fwd_tiles, mode, n, block_size, tile_m, tile_n, qhalf, qt)
+
+
+def bdattn_bwd_tiles(mode, n, block_size, tile_m, tile_n, khalf, kt):
+    """[(query_half, query_tile, masked)] that see key tile kt of half khalf."""
+    return _tiles(lib().bdattn_bwd_tiles, mode, n, block_size, tile_m, tile_n, khalf, kt)
+
+
+def bdattn_row_interval(mode, n, block_size, qhalf, p, khalf):
+    lo, hi = ctypes.c_int32(), ctypes.c_int32()
+    if lib().bdattn_row_interval(mode, n, block_size, qhalf, p, khalf, ctypes.byref(lo), ctypes.byref(hi)) != 0:
+        raise ValueError("bad geometry arguments")
+    return lo.value, hi.value
+
+
+def bdattn_visible_pairs(mode, n, block_size) -> int:
+    r = lib().bdattn_visible_pairs(mode, n, block_size)
+    if r < 0:
+        raise ValueError("bad geometry arguments")
+    return int(r)

@@ -1,0 +1,89 @@
+"""PyTorch-facing functions built on the C-ABI binding.
+
+``diffusion_attn_func(q, k, v, block_size)`` takes q, k, v of shape
+(batch, 2n, heads, headdim) laid out [noisy | clean] (Fast Diffusion
+Attention, "TL;DR": the same call shape as flash-attention's function, with
+a block size where the causal flag would be) and returns the attention
+output; its backward runs the library's backward kernels.  PyTorch only
+allocates the outputs and the workspace and supplies the stream.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _binding as _b
+
+
+def _prep(x: torch.Tensor) -> torch.Tensor:
+    return x if x.is_contiguous() else x.contiguous()
+
+
+class _DiffusionAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, block_size, scale):
+        q, k, v = _prep(q), _prep(k), _prep(v)
+        B, T, H, D = q.shape
+        if T % 2:
+            raise ValueError("the sequence length must be 2n ([noisy | clean])")
+        n = T // 2
+        out = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        _b.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, block_size, scale)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.block_size, ctx.scale = block_size, scale
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse = ctx.saved_tensors
+        dout = _prep(dout)
+        B, T, H, D = q.shape
+        n = T // 2
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = _b.diffusion_attn_bwd_workspace_size(B, n, H, D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        _b.diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, ctx.block_size,
+                              ctx.scale, ws, ws_bytes)
+        return dq, dk, dv, None, None
+
+
+class _CausalAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, scale):
+        q, k, v = _prep(q), _prep(k), _prep(v)
+        B, S, H, D = q.shape
+        out = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+        _b.causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.scale = scale
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse = ctx.saved_tensors
+        dout = _prep(dout)
+        B, S, H, D = q.shape
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = _b.causal_attn_bwd_workspace_size(B, S, H, D)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        _b.causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, ctx.scale, ws, ws_bytes)
+        return dq, dk, dv, None
+
+
+def diffusion_attn_func(q, k, v, block_size: int, softmax_scale=None, return_lse: bool = False):
+    """Block-diffusion attention; q, k, v: (batch, 2n, heads, headdim) bf16."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    out, lse = _DiffusionAttn.apply(q, k, v, int(block_size), scale)
+    return (out, lse) if return_lse else out
+
+
+def causal_attn_func(q, k, v, softmax_scale=None, return_lse: bool = False):
+    """Causal attention (the yardstick); q, k, v: (batch, seq, heads, headdim) bf16."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    out, lse = _CausalAttn.apply(q, k, v, scale)
+    return (out, lse) if return_lse else out

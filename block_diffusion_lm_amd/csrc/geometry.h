@@ -1,0 +1,164 @@
+// geometry.h -- visible intervals and tile enumeration of the block-diffusion
+// mask (and of the causal yardstick), shared by the kernels and by the host
+// inspection entry points.
+//
+// Fast Diffusion Attention, "Block diffusion in one picture": a sample is
+// [noisy | clean], each half of n tokens cut into consecutive blocks of b
+// tokens (the last one shorter when b does not divide n).  A noisy query in
+// block i sees the noisy keys of block i and the clean keys of blocks < i;
+// a clean query in block i sees the clean keys of blocks <= i; a clean query
+// sees no noisy key.  "Visit only the visible tiles": every half is tiled on
+// its own, and a query tile only touches the key tiles that meet its rows'
+// visible intervals (and, in the backward pass, a key tile only the query
+// tiles whose rows see it); only tiles that some invisible pair crosses
+// apply the mask element by element.
+//
+// Positions p are indices inside a half, 0 <= p < n.  The causal yardstick
+// is a single half of length n ("clean") with block size 1, so that query p
+// sees keys [0, p + 1).
+//
+// All visible intervals are of the form [lo(p), hi(p)) with lo and hi
+// non-decreasing in the query row p, and the union over consecutive rows is
+// contiguous; the rectangle classification below relies on both.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define BD_HD __host__ __device__ __forceinline__
+#else
+#define BD_HD static inline
+#endif
+
+namespace bd {
+
+enum : int { MODE_DIFFUSION = 0, MODE_CAUSAL = 1 };
+enum : int { NOISY = 0, CLEAN = 1 };
+enum : int { TILE_SKIP = 0, TILE_FULL = 1, TILE_PARTIAL = 2 };
+
+struct Geom {
+  int n;  // half length (diffusion) or sequence length (causal)
+  int b;  // block size; 1 for causal
+
+  BD_HD int bstart(int p) const { return (p / b) * b; }
+  BD_HD int bend(int p) const {
+    int s = (p / b) * b;
+    return (b >= n - s) ? n : s + b;
+  }
+};
+
+// Visible keys of query row p (half qh) inside key half kh: [lo, hi).
+BD_HD void row_interval(const Geom& g, int qh, int kh, int p, int& lo, int& hi) {
+  if (qh == NOISY && kh == NOISY) {        // own noisy block, both directions
+    lo = g.bstart(p);
+    hi = g.bend(p);
+  } else if (qh == NOISY) {                 // clean blocks strictly before own block
+    lo = 0;
+    hi = g.bstart(p);
+  } else if (kh == CLEAN) {                 // clean blocks up to and including own block
+    lo = 0;
+    hi = g.bend(p);
+  } else {                                  // clean rows see no noisy key
+    lo = 0;
+    hi = 0;
+  }
+}
+
+// Query rows of half qh that see key c of half kh: [lo, hi).
+BD_HD void col_interval(const Geom& g, int qh, int kh, int c, int& lo, int& hi) {
+  if (kh == NOISY && qh == NOISY) {
+    lo = g.bstart(c);
+    hi = g.bend(c);
+  } else if (kh == CLEAN && qh == NOISY) {  // noisy rows of later blocks
+    lo = g.bend(c);
+    hi = g.n;
+  } else if (kh == CLEAN) {                 // clean rows of the same or later blocks
+    lo = g.bstart(c);
+    hi = g.n;
+  } else {
+    lo = 0;
+    hi = 0;
+  }
+}
+
+// Classify the rectangle rows [r0, r1) x keys [c0, c1) (r0 < r1 <= n,
+// c0 < c1; c1 may pass n for a ragged last tile, and keys >= n count as
+// invisible).  Monotone intervals make the rows r0 and r1 - 1 decisive.
+BD_HD int classify(const Geom& g, int qh, int kh, int r0, int r1, int c0, int c1) {
+  int lo_first, hi_first, lo_last, hi_last;
+  row_interval(g, qh, kh, r0, lo_first, hi_first);
+  row_interval(g, qh, kh, r1 - 1, lo_last, hi_last);
+  if (c0 >= hi_last || c1 <= lo_first) return TILE_SKIP;
+  if (lo_last <= c0 && c1 <= hi_first) return TILE_FULL;
+  return TILE_PARTIAL;
+}
+
+BD_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Forward enumeration: the key tiles (of tn keys) visited by query tile qt
+// (of tm rows) of half qh.  At most two segments, each a contiguous range of
+// key tiles in one key half.  For noisy rows the noisy segment (the block
+// diagonal) comes first, then the clean context.
+struct Segments {
+  int count;
+  int half[2];
+  int begin[2];
+  int end[2];
+};
+
+BD_HD Segments fwd_segments(const Geom& g, int mode, int qh, int qt, int tm, int tn) {
+  Segments s;
+  s.count = 0;
+  int r0 = qt * tm;
+  int r1 = (tm >= g.n - r0) ? g.n : r0 + tm;
+  int halves[2] = {NOISY, CLEAN};
+  int nh = 2;
+  if (mode == MODE_CAUSAL || qh == CLEAN) {
+    halves[0] = CLEAN;
+    nh = 1;
+  }
+  for (int i = 0; i < nh; ++i) {
+    int kh = halves[i];
+    int lo_first, hi_first, lo_last, hi_last;
+    row_interval(g, qh, kh, r0, lo_first, hi_first);
+    row_interval(g, qh, kh, r1 - 1, lo_last, hi_last);
+    if (hi_last <= lo_first) continue;      // the rows see nothing of this half
+    s.half[s.count] = kh;
+    s.begin[s.count] = lo_first / tn;
+    s.end[s.count] = ceil_div(hi_last, tn);
+    ++s.count;
+  }
+  return s;
+}
+
+// Backward enumeration: the query tiles (of tm rows) that see key tile kt
+// (of tn keys) of half kh.  Clean keys are seen by clean rows first, then by
+// noisy rows of later blocks; noisy keys only by noisy rows of their block.
+BD_HD Segments bwd_segments(const Geom& g, int mode, int kh, int kt, int tm, int tn) {
+  Segments s;
+  s.count = 0;
+  int c0 = kt * tn;
+  int c1 = (tn >= g.n - c0) ? g.n : c0 + tn;
+  int halves[2] = {CLEAN, NOISY};
+  int nh = 2;
+  if (mode == MODE_CAUSAL) {
+    nh = 1;
+  } else if (kh == NOISY) {
+    halves[0] = NOISY;
+    nh = 1;
+  }
+  for (int i = 0; i < nh; ++i) {
+    int qh = halves[i];
+    int lo_first, hi_first, lo_last, hi_last;
+    col_interval(g, qh, kh, c0, lo_first, hi_first);
+    col_interval(g, qh, kh, c1 - 1, lo_last, hi_last);
+    if (hi_last <= lo_first) continue;
+    s.half[s.count] = qh;
+    s.begin[s.count] = lo_first / tm;
+    s.end[s.count] = ceil_div(hi_last, tm);
+    ++s.count;
+  }
+  return s;
+}
+
+}  // namespace bd

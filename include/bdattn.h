@@ -1,0 +1,166 @@
+/*
+ * bdattn.h -- C ABI of the block-diffusion attention library (libbdattn.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Fast Diffusion Attention, sections "TL;DR" and "Block
+ * diffusion in one picture"): exact softmax attention over a sequence of 2n
+ * tokens laid out as [noisy | clean], under the block-diffusion mask of
+ * block size b.  Blocks are consecutive runs of b tokens from the start of
+ * each half (the last block of a half is shorter when b does not divide n).
+ * A noisy block attends to itself in both directions and to every clean
+ * block strictly before it; a clean block attends to itself and to the
+ * clean blocks before it; every other (query, key) pair is masked.
+ *
+ * The causal entry points compute top-left causal attention (query i sees
+ * keys 0..i of its own sequence) with the same tile engine.  Viewing a
+ * [B, 2n, H, D] tensor as [2B, n, H, D] gives the equal-work yardstick of
+ * "The right yardstick" section.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are caller-owned device memory, contiguous, 16-byte aligned.
+ *    q, k, v, out, dout, dq, dk, dv: bfloat16, layout [B][T][H][D] with
+ *    T = 2n (diffusion) or S (causal); the last dimension is contiguous.
+ *  - lse: float32, layout [B][H][T]: the natural-log log-sum-exp of each
+ *    query row's scaled scores (FlashAttention: Exact Attention Without
+ *    Materialization, section 4.5: the statistic saved for the backward).
+ *  - scale multiplies q.k before the softmax (callers usually pass
+ *    1/sqrt(D)).  It must be finite and nonzero.
+ *  - D must be 64 or 128.  B, n (or S), H >= 1.  block_size >= 1; a block
+ *    longer than a half is allowed (one block per half).
+ *  - stream is a hipStream_t (NULL: the default stream).  Every call is
+ *    asynchronous on that stream; faults during execution surface at the
+ *    caller's next synchronisation.
+ *  - Arguments are validated before anything is launched; on error nothing
+ *    is written and nothing is launched.  The library allocates no memory
+ *    and keeps no state between calls, so calls are reentrant.
+ *  - Return value: one of the BDATTN_* status codes below.
+ *
+ * Outputs are bfloat16 (the inputs' type); accumulation is float32.
+ */
+#ifndef BDATTN_H
+#define BDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  BDATTN_OK = 0,
+  BDATTN_ERR_INVALID = 1,      /* null pointer, misaligned pointer, bad size or scale */
+  BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64 or 128 */
+  BDATTN_ERR_LAUNCH = 3,       /* the HIP runtime refused a launch */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* bdattn_status_string(int status);
+
+/*
+ * Forward pass under the block-diffusion mask.
+ *   q, k, v : [B][2n][H][D] bf16, tokens 0..n-1 noisy, n..2n-1 clean (read)
+ *   out     : [B][2n][H][D] bf16 (written)
+ *   lse     : [B][H][2n]   fp32 (written), natural log, includes scale
+ * Only key tiles that intersect the mask are read; tiles on a block
+ * boundary apply the mask element by element (Fast Diffusion Attention,
+ * "Visit only the visible tiles").
+ */
+int diffusion_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int n, int H, int D, int block_size, float scale, void* stream);
+
+/* Bytes of device workspace diffusion_attn_bwd needs (the per-row
+ * delta_i = dout_i . out_i, float32 [B][H][2n]).  Returns 0 on bad sizes. */
+size_t diffusion_attn_bwd_workspace_size(int B, int n, int H, int D);
+
+/*
+ * Backward pass under the block-diffusion mask (FlashAttention: Exact
+ * Attention Without Materialization, section 4.5: the probabilities are
+ * recomputed from q, k and the saved lse instead of being stored).
+ *   q, k, v, out : as produced/consumed by diffusion_attn_fwd (read)
+ *   dout         : [B][2n][H][D] bf16, gradient of the loss w.r.t. out (read)
+ *   lse          : [B][H][2n] fp32 from diffusion_attn_fwd (read)
+ *   dq, dk, dv   : [B][2n][H][D] bf16 (written, fully overwritten)
+ *   workspace    : device memory of at least
+ *                  diffusion_attn_bwd_workspace_size(B, n, H, D) bytes,
+ *                  16-byte aligned; its contents on entry are ignored.
+ * dK/dV are produced by a key-major pass over the query tiles that see each
+ * key tile, dQ by a separate query-major pass; neither uses atomics, so the
+ * result is bitwise reproducible.
+ */
+int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       int B, int n, int H, int D, int block_size, float scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One stage of the backward pass (same arguments as diffusion_attn_bwd /
+ * causal_attn_bwd; mode 0 = diffusion with block_size, 1 = causal with n = S
+ * and block_size ignored):
+ *   stage 0 -- writes the per-row delta_i = dout_i . out_i to the workspace;
+ *   stage 1 -- dK and dV (reads the workspace);
+ *   stage 2 -- dQ (reads the workspace).
+ * The full backward is stages 0, 1, 2 on one stream.  Stages 1 and 2 read
+ * only inputs and the workspace and write disjoint outputs, so after stage 0
+ * they may run concurrently on two streams.
+ */
+int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
+                     const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, int B, int n, int H, int D, int block_size, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Causal yardstick forward: q, k, v, out [B][S][H][D] bf16, lse [B][H][S] fp32. */
+int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int S, int H, int D, float scale, void* stream);
+
+/* Workspace bytes of causal_attn_bwd (float32 [B][H][S]). */
+size_t causal_attn_bwd_workspace_size(int B, int S, int H, int D);
+
+/* Causal yardstick backward; arguments as diffusion_attn_bwd with T = S. */
+int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    int B, int S, int H, int D, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side inspection of the tile enumeration the kernels use (pure integer
+ * logic, no GPU needed).  Fast Diffusion Attention, "Visit only the visible
+ * tiles": the halves are tiled independently (no tile covers tokens of both
+ * halves).  Clean query rows only ever need clean key tiles from the start
+ * of the half through their own block; noisy query rows need the clean key
+ * tiles that precede their blocks plus the noisy key tiles that overlap
+ * their own blocks.  Nothing else is visited.
+ *
+ * mode: 0 = diffusion (halves 0 = noisy, 1 = clean), 1 = causal (one
+ * sequence of length n, reported as half 1).  Tiles are tile_m query rows by
+ * tile_n keys, aligned to multiples of their size inside each half.
+ *
+ * bdattn_fwd_tiles lists, for query tile qt of half qhalf, every visited key
+ * tile as 3 int32 entries {key_half, key_tile, masked}; masked = 1 when the
+ * tile needs the element mask (some pair inside it is invisible), 0 when
+ * every pair is visible.  bdattn_bwd_tiles lists, for key tile kt of half
+ * khalf, every query tile that sees it as {query_half, query_tile, masked}.
+ * Both write at most max_entries entries and return the number of visited
+ * tiles (which may exceed max_entries), or -1 on bad arguments.
+ */
+int bdattn_fwd_tiles(int mode, int n, int block_size, int tile_m, int tile_n,
+                     int qhalf, int qt, int32_t* entries, int max_entries);
+int bdattn_bwd_tiles(int mode, int n, int block_size, int tile_m, int tile_n,
+                     int khalf, int kt, int32_t* entries, int max_entries);
+
+/* Visible key interval [lo, hi) of query row p of half qhalf within key half
+ * khalf (positions inside that half); lo == hi when it sees none of it.
+ * Returns 0, or -1 on bad arguments. */
+int bdattn_row_interval(int mode, int n, int block_size, int qhalf, int p, int khalf,
+                        int32_t* lo, int32_t* hi);
+
+/* Visible (query, key) pairs of one (sample, head): the sum over rows of
+ * their visible interval lengths.  -1 on bad arguments. */
+int64_t bdattn_visible_pairs(int mode, int n, int block_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDATTN_H */

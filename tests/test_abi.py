@@ -1,0 +1,101 @@
+"""The C ABI: the library loads, exports every symbol the header declares,
+and rejects bad arguments with a status code before touching the GPU.
+
+No call here reaches a kernel launch: every case fails validation first,
+so these tests run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_lm_amd as bd
+from block_diffusion_lm_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdattn.h")
+
+OK, INVALID, UNSUPPORTED, LAUNCH = 0, 1, 2, 3
+# A fake, 16-byte aligned, non-null address: only ever passed alongside some
+# other invalid argument, so the library rejects the call before using it.
+FAKE = 0x10000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"}
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(_binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (OK, INVALID, UNSUPPORTED, LAUNCH, 99):
+        assert isinstance(bd.status_string(code), str) and bd.status_string(code)
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, n=16, H=1, D=64, b=4, scale=0.125)
+    args.update(kw)
+    return bd.lib().diffusion_attn_fwd(args["q"], args["k"], args["v"], args["out"], args["lse"],
+                                       args["B"], args["n"], args["H"], args["D"], args["b"],
+                                       args["scale"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(v=FAKE + 2), INVALID),
+    (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(H=-1), INVALID), (dict(b=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
+    (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
+])
+def test_fwd_rejects(kw, want):
+    assert _fwd(**kw) == want
+
+
+def _bwd(**kw):
+    args = dict(p=[FAKE] * 9, B=1, n=16, H=1, D=64, b=4, scale=0.125, ws=FAKE, wsb=1 << 20)
+    args.update(kw)
+    return bd.lib().diffusion_attn_bwd(*args["p"], args["B"], args["n"], args["H"], args["D"],
+                                       args["b"], args["scale"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p=[FAKE] * 8 + [None]), INVALID), (dict(ws=None), INVALID), (dict(wsb=4), INVALID),
+    (dict(ws=FAKE + 8), INVALID), (dict(B=0), INVALID), (dict(b=-3), INVALID),
+    (dict(scale=float("-inf")), INVALID), (dict(D=32), UNSUPPORTED),
+])
+def test_bwd_rejects(kw, want):
+    assert _bwd(**kw) == want
+
+
+def test_causal_rejects():
+    lib = bd.lib()
+    assert lib.causal_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 64, 0.1, None) == INVALID
+    assert lib.causal_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 1, 64, 0.1, None) == INVALID
+    assert lib.causal_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 80, 0.1, None) == UNSUPPORTED
+    assert lib.causal_attn_bwd(*([FAKE] * 9), 1, 8, 1, 64, 0.1, FAKE, 0, None) == INVALID
+
+
+def test_workspace_sizes():
+    # one float32 per query row, rounded up to 256 bytes
+    assert bd.diffusion_attn_bwd_workspace_size(2, 100, 3, 64) == -(-2 * 3 * 200 * 4 // 256) * 256
+    assert bd.causal_attn_bwd_workspace_size(4, 64, 2, 128) == 4 * 2 * 64 * 4
+    assert bd.diffusion_attn_bwd_workspace_size(0, 100, 3, 64) == 0
+    assert bd.diffusion_attn_bwd_workspace_size(1, 100, 3, 80) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        bd.diffusion_attn_fwd(x, x, x, x.clone(), lse, 1, 4, 1, 64, 2, 0.125)

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP path (called through the C ABI) against the float64
+oracle, on identical seeded bf16 inputs.
+
+Tolerances (the stated targets for bf16 inputs with fp32 accumulation):
+  * forward output: max |O - O_ref| <= 1e-2.  Elements whose exact value is
+    2 or more in magnitude cannot meet that in general: rounding the output
+    to bf16 alone may cost half an ulp (up to 2^-7 .. 2^-6 there) and the
+    bf16 probabilities fed to the P.V product add up to 2^-8 |O_ref|.  Those
+    elements are held to halfulp(O_ref) + 2^-8 |O_ref| + 1e-3 instead, and
+    the test reports how many there were;
+  * log-sum-exp: max |LSE - LSE_ref| <= 1e-3;
+  * dq, dk, dv: max |g - g_ref| <= 2e-2 * max |g_ref|; when the exact
+    gradient is identically zero (a half of one token: every row sees only
+    itself, P = 1, dS = 0) the relative bound is 0, and an absolute 1e-5
+    (far below one bf16 ulp of any nonzero gradient here) is used instead.
+Small problems are compared in full.  The full-size workloads run exactly
+as the benchmark launches them (every sample and head on the GPU); the
+oracle then checks whole heads (all rows of O and LSE) and, for the largest
+problem, sampled rows of dQ and sampled key columns of dK / dV.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_diffusion_lm_amd as bd
+from workloads import WORKLOADS, make_inputs, make_workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+FWD_TOL, LSE_TOL, GRAD_REL = 1e-2, 1e-3, 2e-2
+ZERO_GRAD_ABS = 1e-5
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run_diffusion(q, k, v, do, b, scale, bwd=True):
+    """One forward (and backward) through the C ABI; returns CPU tensors."""
+    dev = _dev()
+    B, T, H, D = q.shape
+    n = T // 2
+    q, k, v = (x.to(dev) for x in (q, k, v))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+    res = {"out": out, "lse": lse}
+    if bwd:
+        do = do.to(dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(bd.diffusion_attn_bwd_workspace_size(B, n, H, D), dtype=torch.uint8, device=dev)
+        bd.diffusion_attn_bwd(q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, b, scale, ws)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {key: t.cpu() for key, t in res.items()}
+
+
+def run_causal(q, k, v, do, scale, bwd=True):
+    dev = _dev()
+    B, S, H, D = q.shape
+    q, k, v = (x.to(dev) for x in (q, k, v))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    bd.causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale)
+    res = {"out": out, "lse": lse}
+    if bwd:
+        do = do.to(dev)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(bd.causal_attn_bwd_workspace_size(B, S, H, D), dtype=torch.uint8, device=dev)
+        bd.causal_attn_bwd(q, k, v, out, do, lse, dq, dk, dv, B, S, H, D, scale, ws)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {key: t.cpu() for key, t in res.items()}
+
+
+def _halfulp_bf16(x):
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+def check_fwd(o, lse, o_ref, lse_ref, what):
+    o = oracle.to_f64(o)
+    err = np.abs(o - o_ref)
+    big = np.abs(o_ref) >= 2.0
+    small_err = err[~big].max() if (~big).any() else 0.0
+    assert small_err <= FWD_TOL, f"{what}: forward max-abs error {small_err:.3g} > {FWD_TOL}"
+    if big.any():
+        bound = _halfulp_bf16(o_ref[big]) + 2.0 ** -8 * np.abs(o_ref[big]) + 1e-3
+        assert np.all(err[big] <= bound), f"{what}: large-|O| elements beyond the rounding bound"
+    lerr = np.abs(oracle.to_f64(lse) - lse_ref).max()
+    assert lerr <= LSE_TOL, f"{what}: LSE max-abs error {lerr:.3g} > {LSE_TOL}"
+    print(f"[{what}] fwd max err {err.max():.3g} (|O|>=2 elements: {int(big.sum())}), lse err {lerr:.3g}")
+
+
+def check_grad(g, g_ref, name, what):
+    g = oracle.to_f64(g)
+    scale = np.abs(g_ref).max()
+    err = np.abs(g - g_ref).max()
+    bound = GRAD_REL * scale if scale > 0 else ZERO_GRAD_ABS
+    assert err <= bound, f"{what}: {name} max-abs error {err:.3g} > {bound:.3g} (max |ref| {scale:.3g})"
+    print(f"[{what}] {name} err {err:.3g} (max |ref| {scale:.3g}, rel {err / max(scale, 1e-300):.3g})")
+
+
+def full_oracle(q, k, v, do, b, scale, heads=None):
+    f = lambda x: oracle.to_f64(x)
+    O, L = oracle.batched(oracle.diffusion_forward, f(q), f(k), f(v), b=b, scale=scale, heads=heads)
+    G = oracle.batched(oracle.diffusion_backward, f(q), f(k), f(v), f(do), b=b, scale=scale, heads=heads)
+    return O, L, G
+
+
+def compare_full(res, q, k, v, do, b, scale, what, heads=None):
+    O, L, (dQ, dK, dV) = full_oracle(q, k, v, do, b, scale, heads)
+    if heads is None:
+        sel = lambda x: x
+        selL = lambda x: x
+    else:
+        idx = heads
+        sel = lambda x: np.stack([np.asarray(x)[bi, :, hi] for bi, hi in idx])
+        selL = lambda x: np.stack([np.asarray(x)[bi, hi] for bi, hi in idx])
+    check_fwd(sel(oracle.to_f64(res["out"])), selL(oracle.to_f64(res["lse"])), sel(O), selL(L), what)
+    for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
+        check_grad(sel(oracle.to_f64(res[name])), sel(ref), name, what)
+
+
+# ---------------------------------------------------------------------------
+# Small problems, compared in full: the tiny workload and the edge cases
+# ---------------------------------------------------------------------------
+
+def test_smallest_workload():
+    w = WORKLOADS["c1"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_diffusion(q, k, v, do, w.b, scale)
+    compare_full(res, q, k, v, do, w.b, scale, "c1")
+
+
+EDGE = [(n, b) for n in (1, 7, 100, 129, 300) for b in (1, 3, 16, 64, 127, 200, n, n + 5)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n,b", EDGE)
+def test_edge_shapes(n, b, D):
+    """Ragged halves (n not a multiple of any tile), blocks of 1 token, blocks
+    longer than a half, misaligned blocks."""
+    q, k, v, do = make_inputs(2, n, 3, D, seed=7000 + 31 * n + b + D)
+    scale = 1 / math.sqrt(D)
+    res = run_diffusion(q, k, v, do, b, scale)
+    compare_full(res, q, k, v, do, b, scale, f"n{n} b{b} D{D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S", [1, 7, 129, 300])
+def test_causal_small(S, D):
+    q, k, v, do = make_inputs(3, S, 2, D, seed=8000 + S + D)
+    q, k, v, do = (x[:, :S].contiguous() for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    res = run_causal(q, k, v, do, scale)
+    f = oracle.to_f64
+    O, L = oracle.batched(oracle.causal_forward, f(q), f(k), f(v), scale=scale)
+    dQ, dK, dV = oracle.batched(oracle.causal_backward, f(q), f(k), f(v), f(do), scale=scale)
+    check_fwd(res["out"], res["lse"], O, L, f"causal S{S} D{D}")
+    for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
+        check_grad(res[name], ref, name, f"causal S{S} D{D}")
+
+
+def test_scale_other_than_default():
+    q, k, v, do = make_inputs(1, 70, 2, 64, seed=9001)
+    res = run_diffusion(q, k, v, do, 5, 0.3)
+    compare_full(res, q, k, v, do, 5, 0.3, "scale 0.3")
+
+
+# ---------------------------------------------------------------------------
+# Determinism and the block-size-1 / causal identity
+# ---------------------------------------------------------------------------
+
+def test_bitwise_reproducible():
+    w = WORKLOADS["c2"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    a = run_diffusion(q, k, v, do, w.b, scale)
+    b = run_diffusion(q, k, v, do, w.b, scale)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_size_one_clean_half_equals_causal_bitwise(D):
+    """With block size 1 the clean half is causal attention on the clean
+    tokens (Fast Diffusion Attention, "Accuracy"); both entry points run the
+    same tile engine with the same key-tile order, so the clean half of the
+    diffusion result equals the causal kernel's bit for bit."""
+    B, n, H = 2, 300, 3
+    q, k, v, do = make_inputs(B, n, H, D, seed=9100 + D)
+    scale = 1 / math.sqrt(D)
+    d = run_diffusion(q, k, v, do, 1, scale)
+    c = run_causal(*(x[:, n:].contiguous() for x in (q, k, v, do)), scale)
+    assert torch.equal(d["out"][:, n:], c["out"])
+    assert torch.equal(d["lse"][:, :, n:], c["lse"])
+    assert torch.equal(d["dq"][:, n:], c["dq"])
+
+
+def test_autograd_wrapper_matches_entry_points():
+    dev = _dev()
+    q, k, v, do = make_inputs(2, 96, 2, 64, seed=9200)
+    ref = run_diffusion(q, k, v, do, 4, 0.125)
+    tq, tk, tv = (x.to(dev).requires_grad_() for x in (q, k, v))
+    out, lse = bd.diffusion_attn_func(tq, tk, tv, 4, softmax_scale=0.125, return_lse=True)
+    out.backward(do.to(dev))
+    assert torch.equal(out.detach().cpu(), ref["out"])
+    assert torch.equal(lse.cpu(), ref["lse"])
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert torch.equal(t.grad.cpu(), ref[name]), name
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,heads", [("c2", [(0, 0), (1, 5), (2, 10), (3, 15)]),
+                                        ("c3", [(0, 0), (7, 15)])])
+def test_workload_whole_heads(name, heads):
+    w = WORKLOADS[name]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_diffusion(q, k, v, do, w.b, scale)
+    compare_full(res, q, k, v, do, w.b, scale, name, heads=heads)
+
+
+C5 = sorted(n for n in WORKLOADS if n.startswith("c5"))
+
+
+@pytest.mark.parametrize("name", C5)
+def test_block_size_sweep(name):
+    w = WORKLOADS[name]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_diffusion(q, k, v, do, w.b, scale)
+    compare_full(res, q, k, v, do, w.b, scale, name, heads=[(3, 7)])
+
+
+def _sample_positions(n, b, rng, count):
+    s = {0, 1, n - 1, n - 2, min(b, n - 1), max(0, n - b)}
+    for t in (64, 128, 256):
+        for m in range(t, n, t * 7):
+            s.update({m - 1, m})
+    s.update(rng.integers(0, n, size=count).tolist())
+    return sorted(x for x in s if 0 <= x < n)
+
+
+def test_largest_workload_sampled():
+    """The long-sequence workload: all rows of O and LSE of two heads, dQ on
+    sampled rows and dK / dV on sampled key columns of those heads."""
+    w = WORKLOADS["c4"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_diffusion(q, k, v, do, w.b, scale)
+    rng = np.random.default_rng(4)
+    n = w.n
+    for bi, hi in ((0, 0), (1, 31)):
+        f = lambda x: oracle.to_f64(x[bi, :, hi])
+        qh, kh, vh, dh = f(q), f(k), f(v), f(do)
+        O = np.empty((2 * n, w.D))
+        L = np.empty(2 * n)
+        for r0 in range(0, 2 * n, 2048):
+            rows = np.arange(r0, r0 + 2048)
+            O[rows], L[rows] = oracle.diffusion_forward_rows(qh, kh, vh, w.b, scale, rows)
+        tag = f"c4 head ({bi},{hi})"
+        check_fwd(res["out"][bi, :, hi], res["lse"][bi, hi], O, L, tag)
+        pos = _sample_positions(n, w.b, rng, 24)
+        rows = np.array(pos + [n + p for p in pos])
+        dq_ref = oracle.diffusion_grad_q_rows(qh, kh, vh, dh, w.b, scale, rows)
+        check_grad(res["dq"][bi, rows, hi], dq_ref, "dq", tag)
+        dk_ref, dv_ref = oracle.diffusion_grad_kv_cols(qh, kh, vh, dh, O, L, w.b, scale, rows)
+        check_grad(res["dk"][bi, rows, hi], dk_ref, "dk", tag)
+        check_grad(res["dv"][bi, rows, hi], dv_ref, "dv", tag)
+
+
+def test_causal_yardstick_workload():
+    """The equal-work causal problem of the medium workload: 16 sequences of
+    2048 tokens (its two halves per sample), checked on two sequences."""
+    w = WORKLOADS["c3"]
+    q, k, v, do = (x.reshape(2 * w.B, w.n, w.H, w.D) for x in make_workload_inputs(w))
+    scale = 1 / math.sqrt(w.D)
+    res = run_causal(q, k, v, do, scale)
+    f = oracle.to_f64
+    for si, hi in ((0, 0), (15, 9)):
+        O, L = oracle.causal_forward(f(q[si, :, hi]), f(k[si, :, hi]), f(v[si, :, hi]), scale)
+        check_fwd(res["out"][si, :, hi], res["lse"][si, hi], O, L, f"causal c3 seq {si}")
+        dQ, dK, dV = oracle.causal_backward(f(q[si, :, hi]), f(k[si, :, hi]), f(v[si, :, hi]),
+                                            f(do[si, :, hi]), scale)
+        for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
+            check_grad(res[name][si, :, hi], ref, name, f"causal c3 seq {si}")
