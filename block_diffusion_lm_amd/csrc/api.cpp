@@ -27,6 +27,9 @@ int check_shape(int B, int T, int H, int D) {
   if (tiles > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
   const long long rows = (long long)B * T * H;
   if (rows > (1LL << 40)) return BDATTN_ERR_INVALID;
+  // The kernels address one half of one sample (all heads) through a 32-bit
+  // buffer range: T/2 (or T) tokens x H x D bf16 must stay below 2 GiB.
+  if ((long long)T * H * D * 2 >= (1LL << 31)) return BDATTN_ERR_UNSUPPORTED;
   return BDATTN_OK;
 }
 
@@ -70,7 +73,7 @@ int fwd_common(int mode, const void* q, const void* k, const void* v, void* out,
 
 size_t workspace_bytes(int B, int T, int H, int D) {
   if (check_shape(B, T, H, D) != BDATTN_OK) return 0;
-  const size_t bytes = (size_t)B * H * T * sizeof(float);
+  const size_t bytes = 2 * (size_t)B * H * T * sizeof(float);
   return (bytes + 255) / 256 * 256;
 }
 
@@ -97,6 +100,7 @@ int bwd_common(int mode, int stage, const void* q, const void* k, const void* v,
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse_in = lse;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = a.delta + (size_t)B * H * T;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
@@ -182,13 +186,13 @@ static int list_tiles(bool fwd, int mode, int n, int block_size, int tile_m, int
                              : bd::bwd_segments(g, mode, half, tile, tile_m, tile_n);
   int count = 0;
   for (int i = 0; i < s.count; ++i) {
-    for (int t = s.begin[i]; t < s.end[i]; ++t) {
+    for (int t = s.begin(i); t < s.end(i); ++t) {
       int r0, r1, c0, c1, qh, kh;
       if (fwd) {
-        qh = half; kh = s.half[i];
+        qh = half; kh = s.half(i);
         r0 = tile * tile_m; c0 = t * tile_n;
       } else {
-        qh = s.half[i]; kh = half;
+        qh = s.half(i); kh = half;
         r0 = t * tile_m; c0 = tile * tile_n;
       }
       r1 = (tile_m >= n - r0) ? n : r0 + tile_m;
@@ -196,7 +200,7 @@ static int list_tiles(bool fwd, int mode, int n, int block_size, int tile_m, int
       const int cls = bd::classify(g, qh, kh, r0, r1, c0, c1);
       if (cls == bd::TILE_SKIP) continue;
       if (count < max_entries) {
-        entries[3 * count + 0] = s.half[i];
+        entries[3 * count + 0] = s.half(i);
         entries[3 * count + 1] = t;
         entries[3 * count + 2] = cls == bd::TILE_PARTIAL ? 1 : 0;
       }

@@ -1,6 +1,7 @@
 // attn_bwd.hip -- backward pass, split in three kernels:
 //
-//   preprocess : delta_i = dO_i . O_i (float32), the row term of dS;
+//   preprocess : per query row, delta_i = dO_i . O_i and lse_i * log2(e)
+//                (both float32, into the caller's workspace);
 //   dkdv       : one workgroup per 128-key tile; it walks the query tiles
 //                that see its keys and accumulates dV = P^T dO and
 //                dK = scale * dS^T Q in registers;
@@ -15,17 +16,19 @@
 // it (geometry.h, bwd_segments), each query tile exactly the key tiles it
 // sees.  Neither kernel uses atomics, so the result is deterministic.
 //
-// Mapping to gfx950 (MFMA layouts in common.h):
-//  dkdv: each wave owns 32 keys, holding K and V as B operands in registers
-//    for the whole walk.  S = Q K^T and dP = dO V^T come out with one key
-//    per lane and query rows in registers; read with k = query row they are
-//    directly the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
-//    operands (dO^T, Q^T) come from transposed LDS copies.  Q and dO tiles
-//    are double-buffered in LDS in natural and transposed layouts.
-//  dq: each wave owns 32 query rows, holding Q and dO as B operands.
-//    S^T = K Q^T and dP^T = V dO^T give one query per lane (so LSE and delta
-//    are per-lane scalars); dQ^T += K^T dS^T takes K^T from a transposed LDS
-//    copy of the key tile.
+// Mapping to gfx950 (MFMA layouts in common.h, LDS tiles in tile_io.h):
+//  dkdv: each wave owns 32 keys and holds K and V as B operands in
+//    registers for the whole walk.  S = Q K^T and dP = dO V^T come out with
+//    one key per lane and the query rows in registers; read with k = query
+//    row they are directly the B operands of dV^T += dO^T P and
+//    dK^T += Q^T dS, whose A operands come from the natural Q and dO tiles
+//    through transposing LDS reads.
+//  dq: each wave owns 32 query rows and holds Q and dO as B operands.
+//    S^T = K Q^T and dP^T = V dO^T give one query per lane, so the row
+//    statistics are per-lane scalars; dQ^T += K^T dS^T reads K^T from the
+//    natural K tile through transposing reads.
+//  Both stream their tiles with buffer loads that write LDS directly,
+//  double-buffered, one tile ahead.
 #include "common.h"
 #include "geometry.h"
 #include "kernels.h"
@@ -38,8 +41,8 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
 }
 
 // ---------------------------------------------------------------------------
-// delta_i = sum_d dO[i][d] * O[i][d]; one 16-byte chunk per lane, rows of
-// D / 8 lanes reduced with cross-lane shuffles.
+// delta_i = sum_d dO[i][d] * O[i][d] and lse2_i = lse_i * log2(e); one
+// 16-byte chunk per lane, rows of D / 8 lanes reduced with shuffles.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long long rows) {
@@ -59,13 +62,59 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long lo
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (row < rows && c == 0) {
-    // row = (b * T + t) * H + h  ->  delta[(b * H + h) * T + t]
+    // row = (b * T + t) * H + h  ->  statistic index (b * H + h) * T + t
     const long long h = row % a.H;
     const long long bt = row / a.H;
     const long long t = bt % a.T;
     const long long b = bt / a.T;
-    a.delta[(b * a.H + h) * a.T + t] = acc;
+    const long long si = (b * a.H + h) * a.T + t;
+    a.delta[si] = acc;
+    a.lse2[si] = a.lse_in[si] * kLog2e;
   }
+}
+
+// What a query-stationary wave needs about one key half (see attn_fwd.hip).
+struct RowSeg {
+  int lo_f, hi_f, lo_l, hi_l, lo_p, hi_p;
+  rsrc_t rk, rv;
+};
+
+template <int D>
+__device__ __forceinline__ RowSeg make_row_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int pw0,
+                                               int pw1, int p, size_t sample0, size_t rs, int hh,
+                                               uint32_t half_bytes) {
+  RowSeg s;
+  row_interval(g, qh, kh, pw0, s.lo_f, s.hi_f);
+  row_interval(g, qh, kh, max(pw1 - 1, pw0), s.lo_l, s.hi_l);
+  row_interval(g, qh, kh, p, s.lo_p, s.hi_p);
+  const size_t base = (sample0 + half_off(a, kh)) * rs + (size_t)hh * D;
+  s.rk = make_rsrc(a.k + base, half_bytes);
+  s.rv = make_rsrc(a.v + base, half_bytes);
+  return s;
+}
+
+// What a key-stationary wave needs about one query half: the rows that see
+// its first and last keys (query-block classification), the rows that see
+// this lane's key (element mask), and the Q / dO / statistics resources.
+struct ColSeg {
+  int clo_f, chi_f, clo_l, chi_l, clo_p, chi_p;
+  rsrc_t rq, rdo, rl, rd;
+};
+
+template <int D>
+__device__ __forceinline__ ColSeg make_col_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int kw0,
+                                               int kw1, int key, size_t sample0, size_t rs, int hh,
+                                               uint32_t half_bytes, size_t stat_base) {
+  ColSeg s;
+  col_interval(g, qh, kh, kw0, s.clo_f, s.chi_f);
+  col_interval(g, qh, kh, max(kw1 - 1, kw0), s.clo_l, s.chi_l);
+  col_interval(g, qh, kh, key, s.clo_p, s.chi_p);
+  const size_t qb = (sample0 + half_off(a, qh)) * rs + (size_t)hh * D;
+  s.rq = make_rsrc(a.q + qb, half_bytes);
+  s.rdo = make_rsrc(a.dout + qb, half_bytes);
+  s.rl = make_rsrc(a.lse2 + stat_base + half_off(a, qh), (uint32_t)a.n * 4u);
+  s.rd = make_rsrc(a.delta + stat_base + half_off(a, qh), (uint32_t)a.n * 4u);
+  return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -80,20 +129,18 @@ struct DkdvCfg {
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  using QL = TileLoader<BQ, D, NT>;
-  static constexpr int QN_OFF = 0;
-  static constexpr int QT_OFF = QN_OFF + QL::NAT_ELEMS;
-  static constexpr int DN_OFF = QT_OFF + QL::T_ELEMS;
-  static constexpr int DT_OFF = DN_OFF + QL::NAT_ELEMS;
-  static constexpr int BUF16 = DT_OFF + QL::T_ELEMS;  // bf16 elements per buffer
-  static constexpr int FBUF = 2 * BQ;                 // floats per buffer: lse2, delta
+  using Tile = DirectTile<BQ, D, NT>;
+  static constexpr int BUF = 2 * Tile::ELEMS;  // Q then dO
+  static constexpr int FBUF = 2 * BQ;          // lse2 then delta
 };
 
+// D = 128 holds K, V, dK and dV (192 registers per lane) for the whole
+// walk: one wave per SIMD.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
   using C = DkdvCfg<D>;
-  using QL = typename C::QL;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF16];
+  using Tile = typename C::Tile;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
   __shared__ __attribute__((aligned(16))) float fsm[2 * C::FBUF];
 
   const int tid = threadIdx.x;
@@ -121,41 +168,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const Geom g{a.n, a.b};
   const size_t rs = (size_t)a.H * D;
   const size_t sample0 = (size_t)bi * a.T;
-  const int koff = half_off(a, kh);
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const size_t koff = sample0 + half_off(a, kh);
 
   const int k0 = kt * C::BKV;
-  const int kw0 = k0 + 32 * w;          // this wave's first key
+  const int kw0 = k0 + 32 * w;  // this wave's first key
+  const int kw1 = min(kw0 + 32, a.n);
   const bool wave_active = kw0 < a.n;
-  const int key = kw0 + l32;            // this lane's key
-  const bool key_ok = key < a.n;
+  const int key = kw0 + l32;    // this lane's key
 
   // K and V as B operands: lane (key, h2) holds row[16s + 8h2 .. +7].
   bf16x8 kf[C::KS], vf[C::KS];
   {
-    const size_t off = (sample0 + koff + key) * rs + (size_t)hh * D;
+    const rsrc_t rk = make_rsrc(a.k + koff * rs + (size_t)hh * D, half_bytes);
+    const rsrc_t rv = make_rsrc(a.v + koff * rs + (size_t)hh * D, half_bytes);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      kf[s] = as_bf16x8(key_ok ? ld16(a.k + off + 16 * s + 8 * h2) : zero_u32x4());
-      vf[s] = as_bf16x8(key_ok ? ld16(a.v + off + 16 * s + 8 * h2) : zero_u32x4());
+      const uint32_t off = (uint32_t)key * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u;
+      kf[s] = as_bf16x8(buf_ld16(rk, off, 0));
+      vf[s] = as_bf16x8(buf_ld16(rv, off, 0));
     }
   }
 
   const Segments seg = bwd_segments(g, a.mode, kh, kt, C::BQ, C::BKV);
-  const int n0 = seg.count > 0 ? seg.end[0] - seg.begin[0] : 0;
-  const int ntiles = n0 + (seg.count > 1 ? seg.end[1] - seg.begin[1] : 0);
-  auto tile_at = [&](int i, int& qh, int& qt) {
-    if (i < n0) {
-      qh = seg.half[0];
-      qt = seg.begin[0] + i;
-    } else {
-      qh = seg.half[1];
-      qt = seg.begin[1] + (i - n0);
-    }
-  };
-  auto row_base = [&](const uint16_t* t, int qh) {
-    return t + (sample0 + half_off(a, qh)) * rs + (size_t)hh * D;
-  };
+  const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
+  const int ntiles = seg.tiles();
+
+  // Per segment: the rows that see the wave's first/last key (q-block
+  // classification), the rows that see this lane's key (element mask), and
+  // the resources of the query half.
   const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;
+  const ColSeg s0 = make_col_seg<D>(a, g, seg.half0, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
+  const ColSeg s1 = make_col_seg<D>(a, g, seg.half1, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
+
+  auto issue_tile = [&](int i, int buf) {
+    const bool second = i >= n0;
+    const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    const ColSeg& sg = second ? s1 : s0;
+    uint16_t* dst = smem + buf * C::BUF;
+    Tile::load(sg.rq, row_bytes, qt * C::BQ, dst, tid);
+    Tile::load(sg.rdo, row_bytes, qt * C::BQ, dst + Tile::ELEMS, tid);
+    // rows past the half read lse2 = delta = 0; their Q and dO rows are
+    // zero too, so they add nothing to dV or dK
+    if (w == 0) lds_direct4(sg.rl, fsm + buf * C::FBUF, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+    if (w == 1) lds_direct4(sg.rd, fsm + buf * C::FBUF + C::BQ, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+  };
 
   floatx16 dk[C::DB], dv[C::DB];
 #pragma unroll
@@ -164,85 +222,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     dv[i] = zero16();
   }
 
-  QL qload, dload;
-  float st_l = 0.f, st_d = 0.f;  // this thread's lse2 / delta entry (threads < BQ)
-  auto load_tile = [&](int i) {
-    int qh, qt;
-    tile_at(i, qh, qt);
-    qload.load(row_base(a.q, qh), rs, qt * C::BQ, a.n, tid);
-    dload.load(row_base(a.dout, qh), rs, qt * C::BQ, a.n, tid);
-    if (tid < C::BQ) {
-      const int r = qt * C::BQ + tid;
-      const bool ok = r < a.n;
-      const size_t si = stat_base + half_off(a, qh) + r;
-      // rows past the half get LSE = +inf, so their probabilities are 0
-      st_l = ok ? a.lse_in[si] * kLog2e : INFINITY;
-      st_d = ok ? a.delta[si] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* b16 = smem + buf * C::BUF16;
-    qload.store_nat(b16 + C::QN_OFF, tid);
-    qload.store_t(b16 + C::QT_OFF, tid);
-    dload.store_nat(b16 + C::DN_OFF, tid);
-    dload.store_t(b16 + C::DT_OFF, tid);
-    if (tid < C::BQ) {
-      fsm[buf * C::FBUF + tid] = st_l;
-      fsm[buf * C::FBUF + C::BQ + tid] = st_d;
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
-    int qh, qt;
-    tile_at(i, qh, qt);
     const bool more = i + 1 < ntiles;
-    if (more) load_tile(i + 1);
+    if (more) issue_tile(i + 1, (i + 1) & 1);
     const int buf = i & 1;
-    const uint16_t* Qs = smem + buf * C::BUF16 + C::QN_OFF;
-    const uint16_t* Qt = smem + buf * C::BUF16 + C::QT_OFF;
-    const uint16_t* Ds = smem + buf * C::BUF16 + C::DN_OFF;
-    const uint16_t* Dt = smem + buf * C::BUF16 + C::DT_OFF;
+    const uint16_t* Qs = smem + buf * C::BUF;
+    const uint16_t* Ds = Qs + Tile::ELEMS;
     const float* Ls = fsm + buf * C::FBUF;
     const float* Dl = Ls + C::BQ;
 
     if (wave_active) {
-      int clo, chi;  // rows of half qh that see this lane's key
-      col_interval(g, qh, kh, key, clo, chi);
+      const bool second = i >= n0;
+      const ColSeg& sg = second ? s1 : s0;
+      const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+      const int cf = sg.clo_f, hf = sg.chi_f, cl = sg.clo_l, hl = sg.chi_l;
+      const int clo = sg.clo_p, chi = sg.chi_p;
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
         const int r0 = qt * C::BQ + 32 * qb;
-        if (r0 >= a.n) continue;
         const int r1 = min(r0 + 32, a.n);
-        const int cls = classify(g, qh, kh, r0, r1, kw0, kw0 + 32);
-        if (cls == TILE_SKIP) continue;
+        if (r0 >= a.n || r1 <= cf || r0 >= hl) continue;
+        const bool full = r0 >= cl && r1 <= hf;
 
         floatx16 sp = zero16(), dp = zero16();
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-          sp = mfma32(lds_nat<D>(Qs, 32 * qb + l32, 2 * s + h2), kf[s], sp);
-          dp = mfma32(lds_nat<D>(Ds, 32 * qb + l32, 2 * s + h2), vf[s], dp);
+          sp = mfma32(lds_row8<D>(Qs, 32 * qb + l32, 2 * s + h2), kf[s], sp);
+          dp = mfma32(lds_row8<D>(Ds, 32 * qb + l32, 2 * s + h2), vf[s], dp);
         }
         // P = exp2(S * scale * log2 e - LSE * log2 e); dS = P * (dP - delta)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int rl = 32 * qb + 8 * gq + 4 * h2;  // tile-local row of register 4gq
-          const float4 l4 = *reinterpret_cast<const float4*>(Ls + rl);
-          const float4 d4 = *reinterpret_cast<const float4*>(Dl + rl);
+          const int rl_ = 32 * qb + 8 * gq + 4 * h2;  // tile row of register 4gq
+          const float4 l4 = *reinterpret_cast<const float4*>(Ls + rl_);
+          const float4 d4 = *reinterpret_cast<const float4*>(Dl + rl_);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int r = 4 * gq + j;
-            float pr = fast_exp2(sp[r] * a.scale_log2 - lv[j]);
-            if (cls == TILE_PARTIAL) {
-              const int row = qt * C::BQ + rl + j;
-              if (row < clo || row >= chi) pr = 0.f;
+            float pr = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lv[j]));
+            if (!full) {
+              const int row = qt * C::BQ + rl_ + j;
+              pr = (row >= clo && row < chi) ? pr : 0.f;
             }
             sp[r] = pr;
             dp[r] = pr * (dp[r] - dl[j]);
@@ -254,22 +280,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
           const bf16x8 sb = pack_bf16x8(dp, 8 * ks);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const int toff = (32 * db + l32) * QL::T_STRIDE + 32 * qb + 16 * ks + 8 * h2;
-            dv[db] = mfma32(lds_vec(Dt + toff), pb, dv[db]);
-            dk[db] = mfma32(lds_vec(Qt + toff), sb, dk[db]);
+            dv[db] = mfma32(lds_trA<D>(Ds, 32 * qb + 16 * ks, 32 * db, lane), pb, dv[db]);
+            dk[db] = mfma32(lds_trA<D>(Qs, 32 * qb + 16 * ks, 32 * db, lane), sb, dk[db]);
           }
         }
       }
     }
 
-    if (more) store_tile((i + 1) & 1);
+    wait_vmem();
     __syncthreads();
   }
 
   // dK^T / dV^T: lane = key, register r of block db = dimension
   // 32db + 8(r/4) + 4h2 + r%4.
-  if (wave_active && key_ok) {
-    const size_t off = (sample0 + koff + key) * rs + (size_t)hh * D;
+  if (wave_active && key < a.n) {
+    const size_t off = (koff + key) * rs + (size_t)hh * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -297,19 +322,16 @@ struct DqCfg {
   static constexpr int KB = BN / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  using KL = TileLoader<BN, D, NT>;
-  static constexpr int KN_OFF = 0;
-  static constexpr int KT_OFF = KN_OFF + KL::NAT_ELEMS;
-  static constexpr int VN_OFF = KT_OFF + KL::T_ELEMS;
-  static constexpr int BUF = VN_OFF + KL::NAT_ELEMS;
+  using Tile = DirectTile<BN, D, NT>;
+  static constexpr int BUF = 2 * Tile::ELEMS;  // K then V
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a, int qtiles) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) {
   using C = DqCfg<D>;
-  using KL = typename C::KL;
+  using Tile = typename C::Tile;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -331,95 +353,86 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   const size_t rs = (size_t)a.H * D;
   const size_t sample0 = (size_t)bi * a.T;
   const int qoff = half_off(a, qh);
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
   const int pw1 = min(pw0 + 32, a.n);
   const bool wave_active = pw0 < a.n;
   const int p = pw0 + l32;
-  const bool row_ok = p < a.n;
 
+  // Q and dO as B operands; rows past the half read as zero, and so do their
+  // statistics, which makes their dS zero.
   bf16x8 qf[C::KS], gf[C::KS];
+  float lse2, dlt;
   {
-    const size_t off = (sample0 + qoff + p) * rs + (size_t)hh * D;
+    const size_t qb = (sample0 + qoff) * rs + (size_t)hh * D;
+    const rsrc_t rq = make_rsrc(a.q + qb, half_bytes);
+    const rsrc_t rg = make_rsrc(a.dout + qb, half_bytes);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      qf[s] = as_bf16x8(row_ok ? ld16(a.q + off + 16 * s + 8 * h2) : zero_u32x4());
-      gf[s] = as_bf16x8(row_ok ? ld16(a.dout + off + 16 * s + 8 * h2) : zero_u32x4());
+      const uint32_t off = (uint32_t)p * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u;
+      qf[s] = as_bf16x8(buf_ld16(rq, off, 0));
+      gf[s] = as_bf16x8(buf_ld16(rg, off, 0));
     }
+    const size_t sb = ((size_t)bi * a.H + hh) * a.T + qoff;
+    lse2 = buf_ldf(make_rsrc(a.lse2 + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+    dlt = buf_ldf(make_rsrc(a.delta + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
   }
-  const size_t si = ((size_t)bi * a.H + hh) * a.T + qoff + p;
-  const float lse2 = row_ok ? a.lse_in[si] * kLog2e : INFINITY;
-  const float dlt = row_ok ? a.delta[si] : 0.f;
 
   const Segments seg = fwd_segments(g, a.mode, qh, qt, C::BM, BN);
-  const int n0 = seg.count > 0 ? seg.end[0] - seg.begin[0] : 0;
-  const int ntiles = n0 + (seg.count > 1 ? seg.end[1] - seg.begin[1] : 0);
-  auto tile_at = [&](int i, int& kh, int& kt) {
-    if (i < n0) {
-      kh = seg.half[0];
-      kt = seg.begin[0] + i;
-    } else {
-      kh = seg.half[1];
-      kt = seg.begin[1] + (i - n0);
-    }
-  };
-  auto kv_base = [&](const uint16_t* t, int kh) {
-    return t + (sample0 + half_off(a, kh)) * rs + (size_t)hh * D;
+  const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
+  const int ntiles = seg.tiles();
+
+  const RowSeg s0 = make_row_seg<D>(a, g, qh, seg.half0, pw0, pw1, p, sample0, rs, hh, half_bytes);
+  const RowSeg s1 = make_row_seg<D>(a, g, qh, seg.half1, pw0, pw1, p, sample0, rs, hh, half_bytes);
+
+  auto issue_tile = [&](int i, int buf) {
+    const bool second = i >= n0;
+    const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    uint16_t* dst = smem + buf * C::BUF;
+    Tile::load(second ? s1.rk : s0.rk, row_bytes, kt * BN, dst, tid);
+    Tile::load(second ? s1.rv : s0.rv, row_bytes, kt * BN, dst + Tile::ELEMS, tid);
   };
 
   floatx16 dq[C::DB];
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) dq[i] = zero16();
 
-  KL kload, vload;
-  if (ntiles > 0) {
-    int kh, kt;
-    tile_at(0, kh, kt);
-    kload.load(kv_base(a.k, kh), rs, kt * BN, a.n, tid);
-    vload.load(kv_base(a.v, kh), rs, kt * BN, a.n, tid);
-    kload.store_nat(smem + C::KN_OFF, tid);
-    kload.store_t(smem + C::KT_OFF, tid);
-    vload.store_nat(smem + C::VN_OFF, tid);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
-    int kh, kt;
-    tile_at(i, kh, kt);
     const bool more = i + 1 < ntiles;
-    if (more) {
-      int kh2, kt2;
-      tile_at(i + 1, kh2, kt2);
-      kload.load(kv_base(a.k, kh2), rs, kt2 * BN, a.n, tid);
-      vload.load(kv_base(a.v, kh2), rs, kt2 * BN, a.n, tid);
-    }
-    const uint16_t* Ks = smem + (i & 1) * C::BUF + C::KN_OFF;
-    const uint16_t* Kt = smem + (i & 1) * C::BUF + C::KT_OFF;
-    const uint16_t* Vs = smem + (i & 1) * C::BUF + C::VN_OFF;
+    if (more) issue_tile(i + 1, (i + 1) & 1);
+    const uint16_t* Ks = smem + (i & 1) * C::BUF;
+    const uint16_t* Vs = Ks + Tile::ELEMS;
 
     if (wave_active) {
-      const int k0 = kt * BN;
-      int lo, hi;
-      row_interval(g, qh, kh, p, lo, hi);
+      const bool second = i >= n0;
+      const RowSeg& sg = second ? s1 : s0;
+      const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
+      const int lf = sg.lo_f, hf = sg.hi_f, ll = sg.lo_l, hl = sg.hi_l;
+      const int lo = sg.lo_p, hi = sg.hi_p;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int c0 = k0 + 32 * kb;
-        if (c0 >= a.n) continue;
-        const int cls = classify(g, qh, kh, pw0, pw1, c0, c0 + 32);
-        if (cls == TILE_SKIP) continue;
+        if (c0 >= hl || c0 + 32 <= lf) continue;
+        const bool full = ll <= c0 && c0 + 32 <= hf;
         floatx16 sp = zero16(), dp = zero16();
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-          sp = mfma32(lds_nat<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], sp);
-          dp = mfma32(lds_nat<D>(Vs, 32 * kb + l32, 2 * s + h2), gf[s], dp);
+          sp = mfma32(lds_row8<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], sp);
+          dp = mfma32(lds_row8<D>(Vs, 32 * kb + l32, 2 * s + h2), gf[s], dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(sp[r] * a.scale_log2 - lse2);
-          if (cls == TILE_PARTIAL) {
+          float pr = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
+          if (!full) {
             const int kk = c0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (kk < lo || kk >= hi) pr = 0.f;
+            pr = (kk >= lo && kk < hi) ? pr : 0.f;
           }
           dp[r] = pr * (dp[r] - dlt);
         }
@@ -428,21 +441,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           const bf16x8 sb = pack_bf16x8(dp, 8 * ks);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            dq[db] = mfma32(lds_vec(Kt + (32 * db + l32) * KL::T_STRIDE + 32 * kb + 16 * ks + 8 * h2), sb, dq[db]);
+            dq[db] = mfma32(lds_trA<D>(Ks, 32 * kb + 16 * ks, 32 * db, lane), sb, dq[db]);
         }
       }
     }
 
-    if (more) {
-      uint16_t* nb = smem + ((i + 1) & 1) * C::BUF;
-      kload.store_nat(nb + C::KN_OFF, tid);
-      kload.store_t(nb + C::KT_OFF, tid);
-      vload.store_nat(nb + C::VN_OFF, tid);
-    }
+    wait_vmem();
     __syncthreads();
   }
 
-  if (wave_active && row_ok) {
+  if (wave_active && p < a.n) {
     uint16_t* qrow = a.dq + (sample0 + qoff + p) * rs + (size_t)hh * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)

@@ -4,23 +4,30 @@
 // FlashAttention: Exact Attention Without Materialization, sections 4.1,
 // 4.2 and 5.1: a query tile streams the key/value tiles it needs through
 // on-chip memory, keeps a running row maximum m, denominator l and
-// unnormalised output z per row, rescales them by exp(m_old - m_new) when
-// the maximum grows and divides by l at the end; scores and probabilities
-// never reach HBM.  Fast Diffusion Attention, "Visit only the visible
-// tiles": the key tiles come from the block-diffusion enumeration
+// unnormalised output z per row, rescales l and z by exp(m_old - m_new)
+// when the maximum changes, and divides by l at the end; scores and
+// probabilities never reach HBM.  Fast Diffusion Attention, "Visit only the
+// visible tiles": the key tiles come from the block-diffusion enumeration
 // (geometry.h) and only tiles crossing a block boundary are masked.
 //
 // Mapping to gfx950: 4 waves per workgroup, each owning 32 query rows.
-// Scores are computed transposed, S^T = K Q^T (K is the MFMA A operand
-// read from LDS, Q the B operand kept in registers), so that a lane owns
-// one query row and the row statistics need a single cross-half exchange;
-// the probabilities then feed O^T += V^T P^T as the B operand straight from
-// the score registers, with V^T read from a transposed LDS copy.  K/V tiles
-// are double-buffered in LDS with the next tile's global loads in flight
-// during the current tile's math (one barrier per tile).  Inside a tile,
-// every wave classifies each 32-key block against its own rows and skips
-// blocks it cannot see (the per-wave analogue of computing the noisy
+// Scores are computed transposed, S^T = K Q^T: K (A operand) is read from
+// LDS, Q (B operand) stays in registers, and each lane owns one query row,
+// so the row statistics need a single exchange between the wave's halves.
+// The probabilities then feed O^T += V^T P^T as the B operand directly from
+// the score registers; V^T comes from the natural V tile through
+// transposing LDS reads.  K/V tiles are double-buffered in LDS and filled
+// by buffer loads that write LDS directly, issued one tile ahead.  Every
+// wave classifies each 32-key block of a tile against its own rows and
+// skips blocks it cannot see (the per-wave analogue of computing the noisy
 // diagonal at reduced width).
+//
+// The running maximum is raised lazily: z and l are rescaled only when a
+// row's maximum grows by more than 2^8 (in base-2 units), otherwise the old
+// maximum stays the reference and probabilities up to 2^8 are accumulated.
+// Because z and l always share one reference, the result is the same
+// function (section 4.2's recurrence holds for any common reference); this
+// removes the per-tile rescale of z in the common case.
 #include "common.h"
 #include "geometry.h"
 #include "kernels.h"
@@ -36,21 +43,43 @@ struct FwdCfg {
   static constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
   static constexpr int DB = D / 32;   // 32-wide column blocks of the head dimension
   static constexpr int KB = BN / 32;  // 32-key blocks per key tile
-  using KL = TileLoader<BN, D, NT>;
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = KL::NAT_ELEMS;
-  static constexpr int BUF = KL::NAT_ELEMS + KL::T_ELEMS;  // elements per buffer
+  using Tile = DirectTile<BN, D, NT>;
+  static constexpr int BUF = 2 * Tile::ELEMS;  // K then V
 };
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 __device__ __forceinline__ int half_offset(const AttnArgs& a, int half) {
   return (a.mode == MODE_DIFFUSION && half == CLEAN) ? a.n : 0;
 }
 
+// What a query-stationary wave needs about one key half: the visible
+// intervals of its first and last rows (block classification), of this
+// lane's row (element mask), and the K / V resources of that half.
+struct RowSeg {
+  int lo_f, hi_f, lo_l, hi_l, lo_p, hi_p;
+  rsrc_t rk, rv;
+};
+
+template <int D>
+__device__ __forceinline__ RowSeg make_row_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int pw0,
+                                               int pw1, int p, size_t sample0, size_t rs, int hh,
+                                               uint32_t half_bytes) {
+  RowSeg s;
+  row_interval(g, qh, kh, pw0, s.lo_f, s.hi_f);
+  row_interval(g, qh, kh, max(pw1 - 1, pw0), s.lo_l, s.hi_l);
+  row_interval(g, qh, kh, p, s.lo_p, s.hi_p);
+  const size_t base = (sample0 + half_offset(a, kh)) * rs + (size_t)hh * D;
+  s.rk = make_rsrc(a.k + base, half_bytes);
+  s.rv = make_rsrc(a.v + base, half_bytes);
+  return s;
+}
+
 template <int D, int BN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN>;
-  using KL = typename C::KL;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+  using Tile = typename C::Tile;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,120 +105,116 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
   const size_t rs = (size_t)a.H * D;
   const size_t sample0 = (size_t)bi * a.T;
   const int qoff = half_offset(a, qh);
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
   const int pw1 = min(pw0 + 32, a.n);
   const bool wave_active = pw0 < a.n;
   const int p = pw0 + l32;
-  const bool row_ok = p < a.n;
 
-  // Q^T operand: lane (row p, half h2) holds Q[p][16s + 8h2 .. +7].
+  // Q^T operand: lane (row p, half h2) holds Q[p][16s + 8h2 .. +7]; rows past
+  // the half read as zero.  A negative scale is folded into Q (exact in
+  // bf16) so that the softmax below always works with a positive factor.
   bf16x8 qf[C::KS];
   {
-    const uint16_t* qrow = a.q + (sample0 + qoff + p) * rs + (size_t)hh * D;
+    const rsrc_t rq = make_rsrc(a.q + (sample0 + qoff) * rs + (size_t)hh * D, half_bytes);
+    const uint32_t flip = a.scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      qf[s] = as_bf16x8(row_ok ? ld16(qrow + 16 * s + 8 * h2) : zero_u32x4());
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 v = buf_ld16(rq, (uint32_t)p * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0);
+      v ^= flip;
+      qf[s] = as_bf16x8(v);
+    }
   }
+  const float cs = fabsf(a.scale) * kLog2e;
 
   const Segments seg = fwd_segments(g, a.mode, qh, qt, C::BM, BN);
-  const int n0 = seg.count > 0 ? seg.end[0] - seg.begin[0] : 0;
-  const int ntiles = n0 + (seg.count > 1 ? seg.end[1] - seg.begin[1] : 0);
+  const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
+  const int ntiles = seg.tiles();
 
-  auto tile_at = [&](int i, int& kh, int& kt) {
-    if (i < n0) {
-      kh = seg.half[0];
-      kt = seg.begin[0] + i;
-    } else {
-      kh = seg.half[1];
-      kt = seg.begin[1] + (i - n0);
-    }
-  };
-  auto kv_base = [&](const uint16_t* t, int kh) {
-    return t + (sample0 + half_offset(a, kh)) * rs + (size_t)hh * D;
+  // Per segment: the wave's first/last row intervals (block classification),
+  // this lane's interval (element mask) and the K/V resources.
+  const RowSeg s0 = make_row_seg<D>(a, g, qh, seg.half0, pw0, pw1, p, sample0, rs, hh, half_bytes);
+  const RowSeg s1 = make_row_seg<D>(a, g, qh, seg.half1, pw0, pw1, p, sample0, rs, hh, half_bytes);
+
+  auto issue_tile = [&](int i, int buf) {
+    const bool second = i >= n0;
+    const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    uint16_t* dst = smem + buf * C::BUF;
+    Tile::load(second ? s1.rk : s0.rk, row_bytes, kt * BN, dst, tid);
+    Tile::load(second ? s1.rv : s0.rv, row_bytes, kt * BN, dst + Tile::ELEMS, tid);
   };
 
   floatx16 o[C::DB];
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) o[i] = zero16();
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // running maximum, base-2 units, scale applied
+  float l_run = 0.f;        // this lane's share of the denominator
 
-  KL kload, vload;
-  if (ntiles > 0) {
-    int kh, kt;
-    tile_at(0, kh, kt);
-    kload.load(kv_base(a.k, kh), rs, kt * BN, a.n, tid);
-    vload.load(kv_base(a.v, kh), rs, kt * BN, a.n, tid);
-    kload.store_nat(smem + C::K_OFF, tid);
-    vload.store_t(smem + C::V_OFF, tid);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
-    int kh, kt;
-    tile_at(i, kh, kt);
     const bool more = i + 1 < ntiles;
-    if (more) {
-      int kh2, kt2;
-      tile_at(i + 1, kh2, kt2);
-      kload.load(kv_base(a.k, kh2), rs, kt2 * BN, a.n, tid);
-      vload.load(kv_base(a.v, kh2), rs, kt2 * BN, a.n, tid);
-    }
-    const uint16_t* Ks = smem + (i & 1) * C::BUF + C::K_OFF;
-    const uint16_t* Vt = smem + (i & 1) * C::BUF + C::V_OFF;
+    if (more) issue_tile(i + 1, (i + 1) & 1);
+    const uint16_t* Ks = smem + (i & 1) * C::BUF;
+    const uint16_t* Vs = Ks + Tile::ELEMS;
 
     if (wave_active) {
-      const int k0 = kt * BN;
-      int lo, hi;
-      row_interval(g, qh, kh, p, lo, hi);
+      const bool second = i >= n0;
+      const RowSeg& sg = second ? s1 : s0;
+      const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
+      const int lf = sg.lo_f, hf = sg.hi_f, ll = sg.lo_l, hl = sg.hi_l;
+      const int lo = sg.lo_p, hi = sg.hi_p;
       int cls[C::KB];
       floatx16 sc[C::KB];
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int c0 = k0 + 32 * kb;
-        cls[kb] = (c0 < a.n) ? classify(g, qh, kh, pw0, pw1, c0, c0 + 32) : TILE_SKIP;
+        cls[kb] = (c0 >= hl || c0 + 32 <= lf) ? TILE_SKIP
+                  : (ll <= c0 && c0 + 32 <= hf) ? TILE_FULL
+                                                : TILE_PARTIAL;
         if (cls[kb] == TILE_SKIP) continue;
         floatx16 acc = zero16();
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s)
-          acc = mfma32(lds_nat<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], acc);
+        for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_row8<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], acc);
         if (cls[kb] == TILE_PARTIAL) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = c0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            float x = acc[r] * a.scale_log2;
-            acc[r] = (key >= lo && key < hi) ? x : -INFINITY;
-            mt = fmaxf(mt, acc[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[r] *= a.scale_log2;
-            mt = fmaxf(mt, acc[r]);
+            acc[r] = (key >= lo && key < hi) ? acc[r] : -INFINITY;
           }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, acc[r]);
         sc[kb] = acc;
       }
-      mt = halves_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
-      l_run *= alpha;
+      // raw scores -> base-2 units with the positive factor cs
+      const float m_tile = halves_max(mt) * cs;
+      const float m_cand = fmaxf(m_run, m_tile);
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleThreshold)) {
+        // 0 when m_run is -inf; 1 for rows whose maximum did not move
+        // (including rows that have seen no key yet, where both are -inf)
+        const float alpha = (m_cand > m_run) ? fast_exp2(m_run - m_cand) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_cand;
+      }
+      const float nbase = (m_run == -INFINITY) ? 0.f : -m_run;
 
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         if (cls[kb] == TILE_SKIP) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(sc[kb][r] - base);
+          const float pr = fast_exp2(__builtin_fmaf(sc[kb][r], cs, nbase));
           sc[kb][r] = pr;
           l_run += pr;
         }
@@ -198,22 +223,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
           const bf16x8 pb = pack_bf16x8(sc[kb], 8 * ks);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            o[db] = mfma32(lds_vec(Vt + (32 * db + l32) * KL::T_STRIDE + 32 * kb + 16 * ks + 8 * h2), pb, o[db]);
+            o[db] = mfma32(lds_trA<D>(Vs, 32 * kb + 16 * ks, 32 * db, lane), pb, o[db]);
         }
       }
     }
 
-    if (more) {
-      uint16_t* nb = smem + ((i + 1) & 1) * C::BUF;
-      kload.store_nat(nb + C::K_OFF, tid);
-      vload.store_t(nb + C::V_OFF, tid);
-    }
+    wait_vmem();
     __syncthreads();
   }
 
-  // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2 (m is in log2 units).
+  // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = halves_sum(l_run);
-  if (wave_active && row_ok) {
+  if (wave_active && p < a.n) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = a.out + (sample0 + qoff + p) * rs + (size_t)hh * D;
 #pragma unroll

@@ -98,36 +98,52 @@ BD_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Forward enumeration: the key tiles (of tn keys) visited by query tile qt
 // (of tm rows) of half qh.  At most two segments, each a contiguous range of
 // key tiles in one key half.  For noisy rows the noisy segment (the block
-// diagonal) comes first, then the clean context.
+// diagonal) comes first, then the clean context.  (Plain fields rather than
+// arrays: a runtime-indexed array here would be placed in memory by the
+// device compiler.)
 struct Segments {
   int count;
-  int half[2];
-  int begin[2];
-  int end[2];
+  int half0, begin0, end0;
+  int half1, begin1, end1;
+  BD_HD int half(int i) const { return i ? half1 : half0; }
+  BD_HD int begin(int i) const { return i ? begin1 : begin0; }
+  BD_HD int end(int i) const { return i ? end1 : end0; }
+  BD_HD int tiles() const { return (count > 0 ? end0 - begin0 : 0) + (count > 1 ? end1 - begin1 : 0); }
 };
 
+// Append the range [begin, end) of half h if it is not empty.
+BD_HD void push_segment(Segments& s, int h, int begin, int end) {
+  if (end <= begin) return;
+  if (s.count == 0) {
+    s.half0 = h;
+    s.begin0 = begin;
+    s.end0 = end;
+  } else {
+    s.half1 = h;
+    s.begin1 = begin;
+    s.end1 = end;
+  }
+  ++s.count;
+}
+
+BD_HD Segments empty_segments() {
+  Segments s = {0, CLEAN, 0, 0, CLEAN, 0, 0};
+  return s;
+}
+
 BD_HD Segments fwd_segments(const Geom& g, int mode, int qh, int qt, int tm, int tn) {
-  Segments s;
-  s.count = 0;
-  int r0 = qt * tm;
-  int r1 = (tm >= g.n - r0) ? g.n : r0 + tm;
-  int halves[2] = {NOISY, CLEAN};
-  int nh = 2;
-  if (mode == MODE_CAUSAL || qh == CLEAN) {
-    halves[0] = CLEAN;
-    nh = 1;
+  Segments s = empty_segments();
+  const int r0 = qt * tm;
+  const int r1 = (tm >= g.n - r0) ? g.n : r0 + tm;
+  int lo_first, hi_first, lo_last, hi_last;
+  if (mode == MODE_DIFFUSION && qh == NOISY) {
+    row_interval(g, qh, NOISY, r0, lo_first, hi_first);
+    row_interval(g, qh, NOISY, r1 - 1, lo_last, hi_last);
+    if (hi_last > lo_first) push_segment(s, NOISY, lo_first / tn, ceil_div(hi_last, tn));
   }
-  for (int i = 0; i < nh; ++i) {
-    int kh = halves[i];
-    int lo_first, hi_first, lo_last, hi_last;
-    row_interval(g, qh, kh, r0, lo_first, hi_first);
-    row_interval(g, qh, kh, r1 - 1, lo_last, hi_last);
-    if (hi_last <= lo_first) continue;      // the rows see nothing of this half
-    s.half[s.count] = kh;
-    s.begin[s.count] = lo_first / tn;
-    s.end[s.count] = ceil_div(hi_last, tn);
-    ++s.count;
-  }
+  row_interval(g, qh, CLEAN, r0, lo_first, hi_first);
+  row_interval(g, qh, CLEAN, r1 - 1, lo_last, hi_last);
+  if (hi_last > lo_first) push_segment(s, CLEAN, lo_first / tn, ceil_div(hi_last, tn));
   return s;
 }
 
@@ -135,28 +151,19 @@ BD_HD Segments fwd_segments(const Geom& g, int mode, int qh, int qt, int tm, int
 // (of tn keys) of half kh.  Clean keys are seen by clean rows first, then by
 // noisy rows of later blocks; noisy keys only by noisy rows of their block.
 BD_HD Segments bwd_segments(const Geom& g, int mode, int kh, int kt, int tm, int tn) {
-  Segments s;
-  s.count = 0;
-  int c0 = kt * tn;
-  int c1 = (tn >= g.n - c0) ? g.n : c0 + tn;
-  int halves[2] = {CLEAN, NOISY};
-  int nh = 2;
-  if (mode == MODE_CAUSAL) {
-    nh = 1;
-  } else if (kh == NOISY) {
-    halves[0] = NOISY;
-    nh = 1;
+  Segments s = empty_segments();
+  const int c0 = kt * tn;
+  const int c1 = (tn >= g.n - c0) ? g.n : c0 + tn;
+  int lo_first, hi_first, lo_last, hi_last;
+  if (mode == MODE_CAUSAL || kh == CLEAN) {
+    col_interval(g, CLEAN, kh, c0, lo_first, hi_first);
+    col_interval(g, CLEAN, kh, c1 - 1, lo_last, hi_last);
+    if (hi_last > lo_first) push_segment(s, CLEAN, lo_first / tm, ceil_div(hi_last, tm));
   }
-  for (int i = 0; i < nh; ++i) {
-    int qh = halves[i];
-    int lo_first, hi_first, lo_last, hi_last;
-    col_interval(g, qh, kh, c0, lo_first, hi_first);
-    col_interval(g, qh, kh, c1 - 1, lo_last, hi_last);
-    if (hi_last <= lo_first) continue;
-    s.half[s.count] = qh;
-    s.begin[s.count] = lo_first / tm;
-    s.end[s.count] = ceil_div(hi_last, tm);
-    ++s.count;
+  if (mode == MODE_DIFFUSION) {
+    col_interval(g, NOISY, kh, c0, lo_first, hi_first);
+    col_interval(g, NOISY, kh, c1 - 1, lo_last, hi_last);
+    if (hi_last > lo_first) push_segment(s, NOISY, lo_first / tm, ceil_div(hi_last, tm));
   }
   return s;
 }

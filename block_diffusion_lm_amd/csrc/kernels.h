@@ -19,7 +19,8 @@ struct AttnArgs {
   float* lse;            // [B][H][T], natural log
   // backward
   const float* lse_in;   // [B][H][T]
-  float* delta;          // workspace [B][H][T]
+  float* delta;          // workspace [B][H][T]: dout_i . out_i
+  float* lse2;           // workspace [B][H][T]: lse * log2(e)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -30,7 +31,7 @@ struct AttnArgs {
   int mode;     // MODE_DIFFUSION / MODE_CAUSAL
   int T;        // tokens per sample: 2n or n
   int nhalves;  // 2 or 1
-  float scale;       // multiplies q.k
+  float scale;       // multiplies q.k (may be negative)
   float scale_log2;  // scale * log2(e)
 };
 

@@ -1,102 +1,85 @@
-// tile_io.h -- moving bf16 tiles of [rows][D] (D contiguous in HBM) into LDS.
+// tile_io.h -- bf16 tiles of [rows][D] (D contiguous in HBM) in LDS.
 //
-// Two LDS layouts are produced from one global read:
-//  * natural:    [rows][D], no padding; the 16-byte chunk c of a row r is
-//                stored at chunk c ^ swz(r).  Both the MFMA operand reads
-//                (8 consecutive rows, same chunk) and the stores of this
-//                loader (rows 4g + j for 8 consecutive g) then hit 8
-//                different 16-byte bank groups.
-//  * transposed: [D][rows + 8], rows contiguous, in the order tpos()
-//                (common.h), so that an MFMA operand whose contraction runs
-//                over the rows is one 16-byte read per lane.
-//
-// Thread unit u covers 4 consecutive rows (4g .. 4g + 3) of one 8-element
-// chunk c, with g varying fastest across lanes: a transposed store of a
-// wave then fills one contiguous run of an LDS row.
+// Tiles are copied from HBM straight into LDS with buffer loads that write
+// LDS directly (no staging registers).  The buffer resource of a tile
+// covers exactly the rows of its half, so rows past the end of the half
+// read as zero.  In LDS a tile is row-major with no padding; the 16-byte
+// chunk c of row r sits at chunk c ^ swz(r).  swz permutes 0..7 over every
+// 8 consecutive rows, which makes two read patterns free of bank conflicts:
+//  * natural operand reads: 8 consecutive rows, one 16-byte chunk each
+//    (ds_read_b128), e.g. K as the A operand of S^T = K Q^T;
+//  * transposing reads (ds_read_b64_tr_b16): a 16-lane group reads 4
+//    consecutive rows x 16 columns (two chunks per row) and every lane
+//    receives the 4 rows of one column.  swz maps the 4 rows to 4 disjoint
+//    chunk pairs.  This yields operands contracted over the tile's rows
+//    (V^T for O^T = V^T P^T, dO^T and Q^T for dV^T, dK^T, K^T for dQ^T)
+//    from the same natural tile.
 #pragma once
 
 #include "common.h"
 
 namespace bd {
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 template <int D>
-__device__ __forceinline__ const uint16_t* nat_ptr(const uint16_t* lds, int row, int chunk) {
-  return lds + row * D + ((chunk ^ swz(row)) << 3);
+__device__ __forceinline__ int nat_off(int row, int chunk) {
+  return row * D + ((chunk ^ swz(row)) << 3);
 }
 
+// 8 elements (16 bytes) of row `row`, chunk `chunk`.
 template <int D>
-__device__ __forceinline__ bf16x8 lds_nat(const uint16_t* lds, int row, int chunk) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(nat_ptr<D>(lds, row, chunk)));
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* t, int row, int chunk) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(t + nat_off<D>(row, chunk)));
 }
 
-__device__ __forceinline__ bf16x8 lds_vec(const uint16_t* p) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+// Transposing read of rows [row0, row0 + 4) (row0 % 4 == 0) and columns
+// [col0, col0 + 16) (col0 % 16 == 0) by the 16-lane group of this lane:
+// lane i of the group receives column col0 + i of the 4 rows.
+template <int D>
+__device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* t, int row0, int col0, int lane) {
+  const int s = lane & 15;
+  const int row = row0 + (s >> 2);
+  const int col = col0 + 4 * (s & 3);
+  const uint16_t* p = t + nat_off<D>(row, col >> 3) + (col & 7);
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int ROWS, int D, int NTHREADS>
-struct TileLoader {
-  static constexpr int G = ROWS / 4;
-  static constexpr int C = D / 8;
-  static constexpr int UNITS = G * C;
-  static constexpr int PER = (UNITS + NTHREADS - 1) / NTHREADS;
-  static constexpr int T_STRIDE = ROWS + 8;
-  static constexpr int NAT_ELEMS = ROWS * D;
-  static constexpr int T_ELEMS = D * T_STRIDE;
+// A operand of a 32x32x16 product contracted over tile rows: lane (l32, h2)
+// gets column col_base + l32 at rows rbase + 4h2 + {0..3} and
+// rbase + 8 + 4h2 + {0..3} -- the row order of the D-layout registers that
+// form the matching B operand (common.h).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_trA(const uint16_t* t, int rbase, int col_base, int lane) {
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int col0 = col_base + (l32 & 16);
+  bf16x4 lo = lds_tr4<D>(t, rbase + 4 * h2, col0, lane);
+  bf16x4 hi = lds_tr4<D>(t, rbase + 8 + 4 * h2, col0, lane);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
-  u32x4 v[PER][4];
+// Copy rows [row0, row0 + ROWS) of a [n][D] view (row stride row_bytes) into
+// an LDS tile, NT threads cooperating; each lane writes 16 bytes and every
+// wave-wide instruction fills 1 KiB of consecutive LDS.
+template <int ROWS, int D, int NT>
+struct DirectTile {
+  static constexpr int CH = D / 8;
+  static constexpr int SLOTS = ROWS * CH;
+  static constexpr int PER = SLOTS / NT;
+  static constexpr int ELEMS = ROWS * D;
+  static_assert(SLOTS % NT == 0, "tile must split evenly over the threads");
 
-  __device__ __forceinline__ static bool active(int u) { return (UNITS % NTHREADS == 0) || u < UNITS; }
-
-  // base: element (row 0, dim 0) of the tile's half for this head; rs: the
-  // token stride in elements; rows >= nvalid (past the end of the half) are
-  // read as zeros.
-  __device__ __forceinline__ void load(const uint16_t* base, size_t rs, int row0, int nvalid, int tid) {
+  __device__ __forceinline__ static void load(rsrc_t src, uint32_t row_bytes, int row0, uint16_t* lds,
+                                              int tid) {
+    const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int u = tid + NTHREADS * i;
-      if (!active(u)) continue;
-      int g = u % G, c = u / G;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int row = row0 + 4 * g + j;
-        v[i][j] = (row < nvalid) ? ld16(base + (size_t)row * rs + c * 8) : zero_u32x4();
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_nat(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + NTHREADS * i;
-      if (!active(u)) continue;
-      int g = u % G, c = u / G;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int row = 4 * g + j;
-        *reinterpret_cast<u32x4*>(lds + row * D + ((c ^ swz(row)) << 3)) = v[i][j];
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_t(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + NTHREADS * i;
-      if (!active(u)) continue;
-      int g = u % G, c = u / G;
-      int pos = tpos(4 * g);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t a0 = v[i][0][w], a1 = v[i][1][w], a2 = v[i][2][w], a3 = v[i][3][w];
-        // dimension 8c + 2w: low 16 bits of each row's word
-        u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        // dimension 8c + 2w + 1: high 16 bits
-        u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(lds + (8 * c + 2 * w) * T_STRIDE + pos) = lo;
-        *reinterpret_cast<u32x2*>(lds + (8 * c + 2 * w + 1) * T_STRIDE + pos) = hi;
-      }
+      const int slot = i * NT + tid;
+      const int r = slot / CH;
+      const int c = (slot % CH) ^ swz(r);
+      const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
+      lds_direct16(src, lds + (i * NT + wbase) * 8, voff, (uint32_t)row0 * row_bytes);
     }
   }
 };

@@ -27,7 +27,9 @@
  *  - scale multiplies q.k before the softmax (callers usually pass
  *    1/sqrt(D)).  It must be finite and nonzero.
  *  - D must be 64 or 128.  B, n (or S), H >= 1.  block_size >= 1; a block
- *    longer than a half is allowed (one block per half).
+ *    longer than a half is allowed (one block per half).  One sample's
+ *    tensor (2n or S tokens x H x D bf16) must be smaller than 2 GiB
+ *    (BDATTN_ERR_UNSUPPORTED otherwise).
  *  - stream is a hipStream_t (NULL: the default stream).  Every call is
  *    asynchronous on that stream; faults during execution surface at the
  *    caller's next synchronisation.
@@ -70,8 +72,9 @@ const char* bdattn_status_string(int status);
 int diffusion_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                        int B, int n, int H, int D, int block_size, float scale, void* stream);
 
-/* Bytes of device workspace diffusion_attn_bwd needs (the per-row
- * delta_i = dout_i . out_i, float32 [B][H][2n]).  Returns 0 on bad sizes. */
+/* Bytes of device workspace diffusion_attn_bwd needs: two float32 values
+ * per query row ([B][H][2n] each), delta_i = dout_i . out_i and the
+ * log-sum-exp in base 2.  Returns 0 on bad sizes. */
 size_t diffusion_attn_bwd_workspace_size(int B, int n, int H, int D);
 
 /*
@@ -98,7 +101,8 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
  * One stage of the backward pass (same arguments as diffusion_attn_bwd /
  * causal_attn_bwd; mode 0 = diffusion with block_size, 1 = causal with n = S
  * and block_size ignored):
- *   stage 0 -- writes the per-row delta_i = dout_i . out_i to the workspace;
+ *   stage 0 -- writes the per-row delta_i = dout_i . out_i and lse_i * log2(e)
+ *              to the workspace;
  *   stage 1 -- dK and dV (reads the workspace);
  *   stage 2 -- dQ (reads the workspace).
  * The full backward is stages 0, 1, 2 on one stream.  Stages 1 and 2 read
@@ -114,7 +118,7 @@ int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const vo
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                     int B, int S, int H, int D, float scale, void* stream);
 
-/* Workspace bytes of causal_attn_bwd (float32 [B][H][S]). */
+/* Workspace bytes of causal_attn_bwd (two float32 [B][H][S] arrays). */
 size_t causal_attn_bwd_workspace_size(int B, int S, int H, int D);
 
 /* Causal yardstick backward; arguments as diffusion_attn_bwd with T = S. */

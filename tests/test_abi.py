@@ -56,6 +56,7 @@ def _fwd(**kw):
     (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(H=-1), INVALID), (dict(b=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
     (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
+    (dict(n=2 ** 22, H=2, D=128), UNSUPPORTED),
 ])
 def test_fwd_rejects(kw, want):
     assert _fwd(**kw) == want
@@ -86,9 +87,9 @@ def test_causal_rejects():
 
 
 def test_workspace_sizes():
-    # one float32 per query row, rounded up to 256 bytes
-    assert bd.diffusion_attn_bwd_workspace_size(2, 100, 3, 64) == -(-2 * 3 * 200 * 4 // 256) * 256
-    assert bd.causal_attn_bwd_workspace_size(4, 64, 2, 128) == 4 * 2 * 64 * 4
+    # two float32 values per query row, rounded up to 256 bytes
+    assert bd.diffusion_attn_bwd_workspace_size(2, 100, 3, 64) == -(-2 * 2 * 3 * 200 * 4 // 256) * 256
+    assert bd.causal_attn_bwd_workspace_size(4, 64, 2, 128) == 2 * 4 * 2 * 64 * 4
     assert bd.diffusion_attn_bwd_workspace_size(0, 100, 3, 64) == 0
     assert bd.diffusion_attn_bwd_workspace_size(1, 100, 3, 80) == 0
 
