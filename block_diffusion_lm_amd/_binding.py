@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbdattn.so")
+# BDATTN_LIB selects another build of the same library (e.g. one compiled
+# with different code-generation options) for side-by-side measurements.
+LIB_PATH = os.environ.get("BDATTN_LIB") or os.path.join(_HERE, "libbdattn.so")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _i32p = ctypes.POINTER(ctypes.c_int32)

@@ -44,8 +44,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libbdattn.so)")
 
 
+# Per-source code-generation options.
+SOURCE_FLAGS = {}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    extra = list(SOURCE_FLAGS.get(src, [])) + list(extra)
     cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,20 +58,32 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = True) -> str:
-    """Compile every source and link libbdattn.so; returns its path."""
+def build(extra_flags=(), verbose: bool = True, out: str = None, source_flags=None) -> str:
+    """Compile every source and link libbdattn.so (or ``out``); returns its path.
+
+    ``source_flags`` maps a source file name to extra hipcc options for that
+    file only (replacing SOURCE_FLAGS for the call)."""
+    global BUILD_DIR
+    lib_path = out or LIB
+    if source_flags is not None:
+        SOURCE_FLAGS.clear()
+        SOURCE_FLAGS.update(source_flags)
+    saved_dir = BUILD_DIR
+    if out:
+        BUILD_DIR = os.path.join(ROOT, "_build", os.path.basename(out) + ".d")
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp"
+    BUILD_DIR = saved_dir
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -311,6 +311,224 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(AttnArg
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV with paired waves.  Holding K, V, dK and dV for 32 keys takes 192
+// registers per lane at D = 128, which leaves one wave per SIMD and no other
+// wave to run while a wave does its softmax arithmetic.  Here the work of a
+// 32-key block is shared by two waves of the workgroup:
+//   wave w     (P-wave)  holds K and dV: S = Q K^T, P, then dV^T += dO^T P;
+//   wave w + 4 (dS-wave) holds V and dK: dP = dO V^T, then with P from the
+//                        P-wave dS = P (dP - delta) and dK^T += Q^T dS.
+// P crosses over through LDS (float32, in the register layout both waves
+// share).  The MFMA work is the same as one wave doing all four products;
+// each wave needs about half the registers, so two waves share each SIMD.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkdvPairCfg {
+  static constexpr int NPAIR = 4;
+  static constexpr int NT = 128 * NPAIR;  // 8 waves
+  static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
+  static constexpr int BQ = 64;           // query rows per streamed tile
+  static constexpr int QB = BQ / 32;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  using Tile = DirectTile<BQ, D, NT>;
+  static constexpr int BUF = 2 * Tile::ELEMS;   // Q then dO
+  static constexpr int FBUF = 2 * BQ;           // lse2 then delta
+  static constexpr int PX = NPAIR * QB * 4 * 64;  // float4 slots of the P exchange
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int ktiles) {
+  using C = DkdvPairCfg<D>;
+  using Tile = typename C::Tile;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) float fsm[2 * C::FBUF];
+  __shared__ __attribute__((aligned(16))) float4 pex[C::PX];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wv & 3;
+  const bool pwave = wv < 4;
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int BH = a.B * a.H;
+  const int bid = blockIdx.x;
+  int kh, kt, bh;
+  if (bid < ktiles * BH) {
+    kh = CLEAN;
+    kt = bid / BH;
+    bh = bid % BH;
+  } else {
+    kh = NOISY;
+    kt = (bid - ktiles * BH) / BH;
+    bh = (bid - ktiles * BH) % BH;
+  }
+  const int bi = bh / a.H;
+  const int hh = bh % a.H;
+  const Geom g{a.n, a.b};
+  const size_t rs = (size_t)a.H * D;
+  const size_t sample0 = (size_t)bi * a.T;
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const size_t koff = sample0 + half_off(a, kh);
+
+  const int kw0 = kt * C::BKV + 32 * pair;  // the pair's first key
+  const int kw1 = min(kw0 + 32, a.n);
+  const bool pair_active = kw0 < a.n;
+  const int key = kw0 + l32;
+
+  // The P-wave holds K, the dS-wave V, as B operands.
+  bf16x8 xf[C::KS];
+  {
+    const rsrc_t rx = make_rsrc((pwave ? a.k : a.v) + koff * rs + (size_t)hh * D, half_bytes);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      xf[s] = as_bf16x8(buf_ld16(rx, (uint32_t)key * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0));
+  }
+
+  const Segments seg = bwd_segments(g, a.mode, kh, kt, C::BQ, C::BKV);
+  const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
+  const int ntiles = seg.tiles();
+  const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;
+  const ColSeg s0 = make_col_seg<D>(a, g, seg.half0, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
+  const ColSeg s1 = make_col_seg<D>(a, g, seg.half1, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
+
+  auto issue_tile = [&](int i, int buf) {
+    const bool second = i >= n0;
+    const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    const ColSeg& sg = second ? s1 : s0;
+    uint16_t* dst = smem + buf * C::BUF;
+    Tile::load(sg.rq, row_bytes, qt * C::BQ, dst, tid);
+    Tile::load(sg.rdo, row_bytes, qt * C::BQ, dst + Tile::ELEMS, tid);
+    // rows past the half read lse2 = delta = 0; their Q and dO rows are
+    // zero too, so they add nothing to dV or dK
+    if (wv == 0) lds_direct4(sg.rl, fsm + buf * C::FBUF, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+    if (wv == 1) lds_direct4(sg.rd, fsm + buf * C::FBUF + C::BQ, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+  };
+
+  floatx16 acc[C::DB];  // dV (P-wave) or dK (dS-wave)
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) acc[i] = zero16();
+
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int i = 0; i < ntiles; ++i) {
+    const bool more = i + 1 < ntiles;
+    if (more) issue_tile(i + 1, (i + 1) & 1);
+    const int buf = i & 1;
+    const uint16_t* Qs = smem + buf * C::BUF;
+    const uint16_t* Ds = Qs + Tile::ELEMS;
+    const float* Ls = fsm + buf * C::FBUF;
+    const float* Dl = Ls + C::BQ;
+
+    const bool second = i >= n0;
+    const ColSeg& sg = second ? s1 : s0;
+    const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    bool act[C::QB], full[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int r0 = qt * C::BQ + 32 * qb;
+      const int r1 = min(r0 + 32, a.n);
+      act[qb] = pair_active && r0 < a.n && r1 > sg.clo_f && r0 < sg.chi_l;
+      full[qb] = r0 >= sg.clo_l && r1 <= sg.chi_f;
+    }
+
+    // Phase 1: S and P (P-wave, which publishes P), dP (dS-wave).
+    bf16x8 pb[C::QB][2];
+    floatx16 dp[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      if (!act[qb]) continue;
+      const uint16_t* X = pwave ? Qs : Ds;
+      floatx16 t = zero16();
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) t = mfma32(lds_row8<D>(X, 32 * qb + l32, 2 * s + h2), xf[s], t);
+      if (pwave) {
+        // P = exp2(S * scale * log2 e - LSE * log2 e), masked off the visible rows
+        float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int rl_ = 32 * qb + 8 * gq + 4 * h2;
+          const float4 l4 = *reinterpret_cast<const float4*>(Ls + rl_);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * gq + j;
+            float pr = fast_exp2(__builtin_fmaf(t[r], a.scale_log2, -lv[j]));
+            if (!full[qb]) {
+              const int row = qt * C::BQ + rl_ + j;
+              pr = (row >= sg.clo_p && row < sg.chi_p) ? pr : 0.f;
+            }
+            t[r] = pr;
+          }
+          px[gq * 64] = make_float4(t[4 * gq], t[4 * gq + 1], t[4 * gq + 2], t[4 * gq + 3]);
+        }
+        pb[qb][0] = pack_bf16x8(t, 0);
+        pb[qb][1] = pack_bf16x8(t, 8);
+      } else {
+        dp[qb] = t;
+      }
+    }
+    __syncthreads();
+
+    // Phase 2: dV^T += dO^T P (P-wave); dS = P (dP - delta), dK^T += Q^T dS (dS-wave).
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      if (!act[qb]) continue;
+      bf16x8 bop[2];
+      if (pwave) {
+        bop[0] = pb[qb][0];
+        bop[1] = pb[qb][1];
+      } else {
+        const float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
+        floatx16 t = dp[qb];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int rl_ = 32 * qb + 8 * gq + 4 * h2;
+          const float4 d4 = *reinterpret_cast<const float4*>(Dl + rl_);
+          const float4 p4 = px[gq * 64];
+          t[4 * gq + 0] = p4.x * (t[4 * gq + 0] - d4.x);
+          t[4 * gq + 1] = p4.y * (t[4 * gq + 1] - d4.y);
+          t[4 * gq + 2] = p4.z * (t[4 * gq + 2] - d4.z);
+          t[4 * gq + 3] = p4.w * (t[4 * gq + 3] - d4.w);
+        }
+        bop[0] = pack_bf16x8(t, 0);
+        bop[1] = pack_bf16x8(t, 8);
+      }
+      const uint16_t* Y = pwave ? Ds : Qs;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = mfma32(lds_trA<D>(Y, 32 * qb + 16 * ks, 32 * db, lane), bop[ks], acc[db]);
+    }
+
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // lane = key, register r of block db = dimension 32db + 8(r/4) + 4h2 + r%4
+  if (pair_active && key < a.n) {
+    const size_t off = (koff + key) * rs + (size_t)hh * D;
+    uint16_t* dst = (pwave ? a.dv : a.dk) + off;
+    const float f = pwave ? 1.f : a.scale;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * h2;
+        u32x2 pk = {pack2_bf16(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
+                    pack2_bf16(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
+        *reinterpret_cast<u32x2*>(dst + d) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: query-stationary.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -472,10 +690,17 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(256), 0, s, a, rows);
   } else if (stage == 1) {
+#ifdef BDATTN_DKDV_FUSED
     using KC = DkdvCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
     const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+#else
+    using KC = DkdvPairCfg<D>;
+    const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
+    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+#endif
   } else {
     using QC = DqCfg<D>;
     const int qtiles = (a.n + QC::BM - 1) / QC::BM;

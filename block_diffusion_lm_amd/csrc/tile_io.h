@@ -20,11 +20,15 @@
 
 namespace bd {
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 template <int D>
 __device__ __forceinline__ int nat_off(int row, int chunk) {
-  return row * D + ((chunk ^ swz(row)) << 3);
+  return row * D + ((chunk ^ swz<D>(row)) << 3);
 }
 
 // 8 elements (16 bytes) of row `row`, chunk `chunk`.
@@ -77,7 +81,7 @@ struct DirectTile {
     for (int i = 0; i < PER; ++i) {
       const int slot = i * NT + tid;
       const int r = slot / CH;
-      const int c = (slot % CH) ^ swz(r);
+      const int c = (slot % CH) ^ swz<D>(r);
       const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
       lds_direct16(src, lds + (i * NT + wbase) * 8, voff, (uint32_t)row0 * row_bytes);
     }
