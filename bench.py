@@ -47,18 +47,20 @@ def parse():
     ap.add_argument("--round-ms", type=float, default=300.0, help="target duration of each phase of a round")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal yardstick rounds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
-                    help="query rows per half in the oracle's timed sample")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time of the oracle's timed sample")
+    ap.add_argument("--profiles", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles"),
+                    help="folder holding traffic_<kernel>_<workload>.txt (HBM bytes per launch)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, q, k, v, do, rows_per_half):
-    """Time the float64 oracle (as it stands) on a bounded sample: a chunk of
-    query rows from each half of one (sample, head), forward and backward."""
+def cpu_baseline(w, q, k, v, do, target_s=10.0, chunk=2048):
+    """Time the float64 oracle (as it stands) on a bounded sample of the same
+    workload: whole (sample, head) pairs, processed in chunks of query rows
+    (forward and backward of each chunk against all 2n keys), until about
+    target_s seconds of CPU work have been done."""
     import numpy as np
     import oracle
     try:
@@ -67,27 +69,44 @@ def cpu_baseline(w, q, k, v, do, rows_per_half):
     except Exception:  # pragma: no cover
         cores = 1
     n, scale = w.n, 1.0 / math.sqrt(w.D)
-    f = lambda x: oracle.to_f64(x[0, :, 0])
-    qh, kh, vh, dh = f(q), f(k), f(v), f(do)
-    r = min(rows_per_half, n)
-    mid = (n - r) // 2
-    rows = np.concatenate([np.arange(mid, mid + r), n + np.arange(mid, mid + r)])
-    M = oracle.block_diffusion_mask(n, w.b, rows)
-    pairs = int(M.sum())
-    t0 = time.perf_counter()
-    oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
-    t1 = time.perf_counter()
-    oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
-    t2 = time.perf_counter()
+    pairs, chunks, heads = 0, 0, 0
+    t_fwd = t_bwd = 0.0
+    t_start = time.perf_counter()
+    done = False
+    for bi in range(w.B):
+        for hi in range(w.H):
+            f = lambda x: oracle.to_f64(x[bi, :, hi])
+            qh, kh, vh, dh = f(q), f(k), f(v), f(do)
+            for r0 in range(0, 2 * n, chunk):
+                rows = np.arange(r0, min(r0 + chunk, 2 * n))
+                M = oracle.block_diffusion_mask(n, w.b, rows)
+                pairs += int(M.sum())
+                t0 = time.perf_counter()
+                oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
+                t1 = time.perf_counter()
+                oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
+                t2 = time.perf_counter()
+                t_fwd += t1 - t0
+                t_bwd += t2 - t1
+                chunks += 1
+                if time.perf_counter() - t_start >= target_s and r0 + chunk >= 2 * n:
+                    done = True
+                    break
+            heads += 1
+            if done:
+                break
+        if done:
+            break
     flops = 3.5 * 4 * pairs * w.D
     return {
-        "value": flops / (t2 - t0) / 1e12,
+        "value": flops / (t_fwd + t_bwd) / 1e12,
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"float64 oracle forward + backward of {2 * r} query rows ({r} per half) of one "
-                   f"(sample, head) of {w.name}, all {2 * n} keys; {pairs} visible pairs; "
-                   f"{t1 - t0:.2f} s forward, {t2 - t1:.2f} s backward; host {platform.processor() or platform.machine()}"),
+        "sample": (f"float64 oracle forward + backward of {heads} whole (sample, head) pair(s) of {w.name} "
+                   f"({chunks} chunks of {chunk} query rows against all {2 * n} keys; {pairs} visible pairs); "
+                   f"{t_fwd:.1f} s forward + {t_bwd:.1f} s backward; BLAS threads {cores}; "
+                   f"host {platform.processor() or platform.machine()}"),
     }
 
 
@@ -193,12 +212,13 @@ def main():
                         "bwd_dq": 3 * 2.0 * P * D * H * B}     # S, dP, dQ
     dom = max(per_kernel_flops, key=lambda kname: kern_avg[kname])
     achieved = per_kernel_flops[dom] / (kern_avg[dom] * 1e-3) / 1e12
+    # HBM bytes per launch from the rocprofv3 counter runs, valid only while
+    # the kernel sources are the ones the counters were taken on
+    from block_diffusion_lm_amd import profiling
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as fh:
-            tr = json.load(fh)
-        if tr.get("kernel") == dom and tr.get("workload") == w.name:
-            traffic = tr.get("bytes_per_launch")
+    tr = profiling.read_traffic(os.path.join(args.profiles, f"traffic_{dom}_{w.name}.txt"))
+    if tr and tr.get("source_sha256") == profiling.source_hash():
+        traffic = float(tr["bytes_per_launch"])
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
                 "algorithmic_flops_per_launch": per_kernel_flops[dom],
@@ -246,7 +266,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_rows)
+        cpu = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
 
     line = {
         "metric": "fwd+bwd TFLOPS (visible pairs only) and ratio vs own causal kernel on 2B×n",
