@@ -73,254 +73,42 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long lo
   }
 }
 
-// What a query-stationary wave needs about one key half (see attn_fwd.hip).
-struct RowSeg {
-  int lo_f, hi_f, lo_l, hi_l, lo_p, hi_p;
-  rsrc_t rk, rv;
-};
+// Per-segment scalars.  A key-stationary wave needs, for each query half it
+// walks: the rows that see its first and last keys (query-block
+// classification), the rows that see this lane's key (element mask), and the
+// offsets of row 0 of Q / dO and of its statistics.  A query-stationary wave
+// needs the visible intervals of its first, last and own rows and the offset
+// of row 0 of K / V.  They are kept as separate scalars and picked with
+// selects: grouped in a struct, the compiler would select between the
+// structs' addresses and keep both in scratch memory.
+#define COL_SEGMENTS                                                          \
+  const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;                    \
+  int clo_f0, chi_f0, clo_l0, chi_l0, clo_p0, chi_p0;                        \
+  int clo_f1, chi_f1, clo_l1, chi_l1, clo_p1, chi_p1;                        \
+  col_interval(g, seg.half0, kh, kw0, clo_f0, chi_f0);                        \
+  col_interval(g, seg.half0, kh, max(kw1 - 1, kw0), clo_l0, chi_l0);          \
+  col_interval(g, seg.half0, kh, key, clo_p0, chi_p0);                        \
+  col_interval(g, seg.half1, kh, kw0, clo_f1, chi_f1);                        \
+  col_interval(g, seg.half1, kh, max(kw1 - 1, kw0), clo_l1, chi_l1);          \
+  col_interval(g, seg.half1, kh, key, clo_p1, chi_p1);                        \
+  const size_t qb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh * D; \
+  const size_t qb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh * D; \
+  const size_t sb0 = stat_base + half_off(a, seg.half0);                      \
+  const size_t sb1 = stat_base + half_off(a, seg.half1);
 
-template <int D>
-__device__ __forceinline__ RowSeg make_row_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int pw0,
-                                               int pw1, int p, size_t sample0, size_t rs, int hh,
-                                               uint32_t half_bytes) {
-  RowSeg s;
-  row_interval(g, qh, kh, pw0, s.lo_f, s.hi_f);
-  row_interval(g, qh, kh, max(pw1 - 1, pw0), s.lo_l, s.hi_l);
-  row_interval(g, qh, kh, p, s.lo_p, s.hi_p);
-  const size_t base = (sample0 + half_off(a, kh)) * rs + (size_t)hh * D;
-  s.rk = make_rsrc(a.k + base, half_bytes);
-  s.rv = make_rsrc(a.v + base, half_bytes);
-  return s;
-}
-
-// What a key-stationary wave needs about one query half: the rows that see
-// its first and last keys (query-block classification), the rows that see
-// this lane's key (element mask), and the Q / dO / statistics resources.
-struct ColSeg {
-  int clo_f, chi_f, clo_l, chi_l, clo_p, chi_p;
-  rsrc_t rq, rdo, rl, rd;
-};
-
-template <int D>
-__device__ __forceinline__ ColSeg make_col_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int kw0,
-                                               int kw1, int key, size_t sample0, size_t rs, int hh,
-                                               uint32_t half_bytes, size_t stat_base) {
-  ColSeg s;
-  col_interval(g, qh, kh, kw0, s.clo_f, s.chi_f);
-  col_interval(g, qh, kh, max(kw1 - 1, kw0), s.clo_l, s.chi_l);
-  col_interval(g, qh, kh, key, s.clo_p, s.chi_p);
-  const size_t qb = (sample0 + half_off(a, qh)) * rs + (size_t)hh * D;
-  s.rq = make_rsrc(a.q + qb, half_bytes);
-  s.rdo = make_rsrc(a.dout + qb, half_bytes);
-  s.rl = make_rsrc(a.lse2 + stat_base + half_off(a, qh), (uint32_t)a.n * 4u);
-  s.rd = make_rsrc(a.delta + stat_base + half_off(a, qh), (uint32_t)a.n * 4u);
-  return s;
-}
+#define ROW_SEGMENTS                                                           \
+  int lo_f0, hi_f0, lo_l0, hi_l0, lo_p0, hi_p0, lo_f1, hi_f1, lo_l1, hi_l1, lo_p1, hi_p1; \
+  row_interval(g, qh, seg.half0, pw0, lo_f0, hi_f0);                            \
+  row_interval(g, qh, seg.half0, max(pw1 - 1, pw0), lo_l0, hi_l0);              \
+  row_interval(g, qh, seg.half0, p, lo_p0, hi_p0);                              \
+  row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);                            \
+  row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);              \
+  row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);                              \
+  const size_t kvb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh * D;  \
+  const size_t kvb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh * D;
 
 // ---------------------------------------------------------------------------
 // dK / dV: key-stationary.
-// ---------------------------------------------------------------------------
-template <int D>
-struct DkdvCfg {
-  static constexpr int NW = 4;
-  static constexpr int NT = 64 * NW;
-  static constexpr int BKV = 32 * NW;  // keys per workgroup
-  static constexpr int BQ = 64;        // query rows per streamed tile
-  static constexpr int QB = BQ / 32;
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-  using Tile = DirectTile<BQ, D, NT>;
-  static constexpr int BUF = 2 * Tile::ELEMS;  // Q then dO
-  static constexpr int FBUF = 2 * BQ;          // lse2 then delta
-};
-
-// D = 128 holds K, V, dK and dV (192 registers per lane) for the whole
-// walk: one wave per SIMD.
-template <int D>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
-  using C = DkdvCfg<D>;
-  using Tile = typename C::Tile;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
-  __shared__ __attribute__((aligned(16))) float fsm[2 * C::FBUF];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int h2 = lane >> 5;
-
-  // Clean key tiles in increasing order (the earliest keys are seen by the
-  // most rows), then the noisy key tiles, which only their own blocks see.
-  const int BH = a.B * a.H;
-  const int bid = blockIdx.x;
-  int kh, kt, bh;
-  if (bid < ktiles * BH) {
-    kh = CLEAN;
-    kt = bid / BH;
-    bh = bid % BH;
-  } else {
-    kh = NOISY;
-    kt = (bid - ktiles * BH) / BH;
-    bh = (bid - ktiles * BH) % BH;
-  }
-  const int bi = bh / a.H;
-  const int hh = bh % a.H;
-  const Geom g{a.n, a.b};
-  const size_t rs = (size_t)a.H * D;
-  const size_t sample0 = (size_t)bi * a.T;
-  const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
-  const size_t koff = sample0 + half_off(a, kh);
-
-  const int k0 = kt * C::BKV;
-  const int kw0 = k0 + 32 * w;  // this wave's first key
-  const int kw1 = min(kw0 + 32, a.n);
-  const bool wave_active = kw0 < a.n;
-  const int key = kw0 + l32;    // this lane's key
-
-  // K and V as B operands: lane (key, h2) holds row[16s + 8h2 .. +7].
-  bf16x8 kf[C::KS], vf[C::KS];
-  {
-    const rsrc_t rk = make_rsrc(a.k + koff * rs + (size_t)hh * D, half_bytes);
-    const rsrc_t rv = make_rsrc(a.v + koff * rs + (size_t)hh * D, half_bytes);
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const uint32_t off = (uint32_t)key * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u;
-      kf[s] = as_bf16x8(buf_ld16(rk, off, 0));
-      vf[s] = as_bf16x8(buf_ld16(rv, off, 0));
-    }
-  }
-
-  const Segments seg = bwd_segments(g, a.mode, kh, kt, C::BQ, C::BKV);
-  const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
-  const int ntiles = seg.tiles();
-
-  // Per segment: the rows that see the wave's first/last key (q-block
-  // classification), the rows that see this lane's key (element mask), and
-  // the resources of the query half.
-  const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;
-  const ColSeg s0 = make_col_seg<D>(a, g, seg.half0, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
-  const ColSeg s1 = make_col_seg<D>(a, g, seg.half1, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
-
-  auto issue_tile = [&](int i, int buf) {
-    const bool second = i >= n0;
-    const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    const ColSeg& sg = second ? s1 : s0;
-    uint16_t* dst = smem + buf * C::BUF;
-    Tile::load(sg.rq, row_bytes, qt * C::BQ, dst, tid);
-    Tile::load(sg.rdo, row_bytes, qt * C::BQ, dst + Tile::ELEMS, tid);
-    // rows past the half read lse2 = delta = 0; their Q and dO rows are
-    // zero too, so they add nothing to dV or dK
-    if (w == 0) lds_direct4(sg.rl, fsm + buf * C::FBUF, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
-    if (w == 1) lds_direct4(sg.rd, fsm + buf * C::FBUF + C::BQ, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
-  };
-
-  floatx16 dk[C::DB], dv[C::DB];
-#pragma unroll
-  for (int i = 0; i < C::DB; ++i) {
-    dk[i] = zero16();
-    dv[i] = zero16();
-  }
-
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
-
-  for (int i = 0; i < ntiles; ++i) {
-    const bool more = i + 1 < ntiles;
-    if (more) issue_tile(i + 1, (i + 1) & 1);
-    const int buf = i & 1;
-    const uint16_t* Qs = smem + buf * C::BUF;
-    const uint16_t* Ds = Qs + Tile::ELEMS;
-    const float* Ls = fsm + buf * C::FBUF;
-    const float* Dl = Ls + C::BQ;
-
-    if (wave_active) {
-      const bool second = i >= n0;
-      const ColSeg& sg = second ? s1 : s0;
-      const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-      const int cf = sg.clo_f, hf = sg.chi_f, cl = sg.clo_l, hl = sg.chi_l;
-      const int clo = sg.clo_p, chi = sg.chi_p;
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-        const int r0 = qt * C::BQ + 32 * qb;
-        const int r1 = min(r0 + 32, a.n);
-        if (r0 >= a.n || r1 <= cf || r0 >= hl) continue;
-        const bool full = r0 >= cl && r1 <= hf;
-
-        floatx16 sp = zero16(), dp = zero16();
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-          sp = mfma32(lds_row8<D>(Qs, 32 * qb + l32, 2 * s + h2), kf[s], sp);
-          dp = mfma32(lds_row8<D>(Ds, 32 * qb + l32, 2 * s + h2), vf[s], dp);
-        }
-        // P = exp2(S * scale * log2 e - LSE * log2 e); dS = P * (dP - delta)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int rl_ = 32 * qb + 8 * gq + 4 * h2;  // tile row of register 4gq
-          const float4 l4 = *reinterpret_cast<const float4*>(Ls + rl_);
-          const float4 d4 = *reinterpret_cast<const float4*>(Dl + rl_);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * gq + j;
-            float pr = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lv[j]));
-            if (!full) {
-              const int row = qt * C::BQ + rl_ + j;
-              pr = (row >= clo && row < chi) ? pr : 0.f;
-            }
-            sp[r] = pr;
-            dp[r] = pr * (dp[r] - dl[j]);
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = pack_bf16x8(sp, 8 * ks);
-          const bf16x8 sb = pack_bf16x8(dp, 8 * ks);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            dv[db] = mfma32(lds_trA<D>(Ds, 32 * qb + 16 * ks, 32 * db, lane), pb, dv[db]);
-            dk[db] = mfma32(lds_trA<D>(Qs, 32 * qb + 16 * ks, 32 * db, lane), sb, dk[db]);
-          }
-        }
-      }
-    }
-
-    wait_vmem();
-    __syncthreads();
-  }
-
-  // dK^T / dV^T: lane = key, register r of block db = dimension
-  // 32db + 8(r/4) + 4h2 + r%4.
-  if (wave_active && key < a.n) {
-    const size_t off = (koff + key) * rs + (size_t)hh * D;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * h2;
-        u32x2 kv = {pack2_bf16(dk[db][4 * gq] * a.scale, dk[db][4 * gq + 1] * a.scale),
-                    pack2_bf16(dk[db][4 * gq + 2] * a.scale, dk[db][4 * gq + 3] * a.scale)};
-        u32x2 vv = {pack2_bf16(dv[db][4 * gq], dv[db][4 * gq + 1]),
-                    pack2_bf16(dv[db][4 * gq + 2], dv[db][4 * gq + 3])};
-        *reinterpret_cast<u32x2*>(a.dk + off + d) = kv;
-        *reinterpret_cast<u32x2*>(a.dv + off + d) = vv;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK / dV with paired waves.  Holding K, V, dK and dV for 32 keys takes 192
-// registers per lane at D = 128, which leaves one wave per SIMD and no other
-// wave to run while a wave does its softmax arithmetic.  Here the work of a
-// 32-key block is shared by two waves of the workgroup:
-//   wave w     (P-wave)  holds K and dV: S = Q K^T, P, then dV^T += dO^T P;
-//   wave w + 4 (dS-wave) holds V and dK: dP = dO V^T, then with P from the
-//                        P-wave dS = P (dP - delta) and dK^T += Q^T dS.
-// P crosses over through LDS (float32, in the register layout both waves
-// share).  The MFMA work is the same as one wave doing all four products;
-// each wave needs about half the registers, so two waves share each SIMD.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvPairCfg {
@@ -344,6 +132,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
   __shared__ __attribute__((aligned(16))) float fsm[2 * C::FBUF];
   __shared__ __attribute__((aligned(16))) float4 pex[C::PX];
+  const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(smem));
+  const uint32_t fbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(fsm));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -386,26 +176,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
       xf[s] = as_bf16x8(buf_ld16(rx, (uint32_t)key * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0));
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) settle(xf[s]);
   }
 
   const Segments seg = bwd_segments(g, a.mode, kh, kt, C::BQ, C::BKV);
   const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
   const int ntiles = seg.tiles();
-  const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;
-  const ColSeg s0 = make_col_seg<D>(a, g, seg.half0, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
-  const ColSeg s1 = make_col_seg<D>(a, g, seg.half1, kh, kw0, kw1, key, sample0, rs, hh, half_bytes, stat_base);
-
-  auto issue_tile = [&](int i, int buf) {
+  COL_SEGMENTS
+  auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
     const bool second = i >= n0;
     const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    const ColSeg& sg = second ? s1 : s0;
-    uint16_t* dst = smem + buf * C::BUF;
-    Tile::load(sg.rq, row_bytes, qt * C::BQ, dst, tid);
-    Tile::load(sg.rdo, row_bytes, qt * C::BQ, dst + Tile::ELEMS, tid);
+    const size_t qb = second ? qb1 : qb0;
+    const size_t sb = second ? sb1 : sb0;
+    const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
+    Tile::load(make_rsrc(a.q + qb, half_bytes), row_bytes, qt * C::BQ, dst, tid);
+    Tile::load(make_rsrc(a.dout + qb, half_bytes), row_bytes, qt * C::BQ, dst + Tile::ELEMS * 2u, tid);
     // rows past the half read lse2 = delta = 0; their Q and dO rows are
     // zero too, so they add nothing to dV or dK
-    if (wv == 0) lds_direct4(sg.rl, fsm + buf * C::FBUF, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
-    if (wv == 1) lds_direct4(sg.rd, fsm + buf * C::FBUF + C::BQ, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+    const uint32_t sbytes = (uint32_t)a.n * 4u;
+    if (wv == 0)
+      lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fbase + (uint32_t)(buf * C::FBUF) * 4u, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+    if (wv == 1)
+      lds_direct4(make_rsrc(a.delta + sb, sbytes), fbase + (uint32_t)(buf * C::FBUF + C::BQ) * 4u, (uint32_t)lane * 4u,
+                  (uint32_t)qt * C::BQ * 4u);
   };
 
   floatx16 acc[C::DB];  // dV (P-wave) or dK (dS-wave)
@@ -426,15 +220,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
     const float* Dl = Ls + C::BQ;
 
     const bool second = i >= n0;
-    const ColSeg& sg = second ? s1 : s0;
     const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+    const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
+    const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
+    const int clo = second ? clo_p1 : clo_p0, chi = second ? chi_p1 : chi_p0;
     bool act[C::QB], full[C::QB];
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const int r0 = qt * C::BQ + 32 * qb;
       const int r1 = min(r0 + 32, a.n);
-      act[qb] = pair_active && r0 < a.n && r1 > sg.clo_f && r0 < sg.chi_l;
-      full[qb] = r0 >= sg.clo_l && r1 <= sg.chi_f;
+      act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
+      full[qb] = r0 >= cl && r1 <= hf;
     }
 
     // Phase 1: S and P (P-wave, which publishes P), dP (dS-wave).
@@ -445,8 +241,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
       if (!act[qb]) continue;
       const uint16_t* X = pwave ? Qs : Ds;
       floatx16 t = zero16();
+      mfma_burst_begin();
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) t = mfma32(lds_row8<D>(X, 32 * qb + l32, 2 * s + h2), xf[s], t);
+      mfma_burst_end();
       if (pwave) {
         // P = exp2(S * scale * log2 e - LSE * log2 e), masked off the visible rows
         float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
@@ -461,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
             float pr = fast_exp2(__builtin_fmaf(t[r], a.scale_log2, -lv[j]));
             if (!full[qb]) {
               const int row = qt * C::BQ + rl_ + j;
-              pr = (row >= sg.clo_p && row < sg.chi_p) ? pr : 0.f;
+              pr = (row >= clo && row < chi) ? pr : 0.f;
             }
             t[r] = pr;
           }
@@ -500,11 +298,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
         bop[1] = pack_bf16x8(t, 8);
       }
       const uint16_t* Y = pwave ? Ds : Qs;
+      mfma_burst_begin();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
           acc[db] = mfma32(lds_trA<D>(Y, 32 * qb + 16 * ks, 32 * db, lane), bop[ks], acc[db]);
+      mfma_burst_end();
     }
 
     wait_vmem();
@@ -550,6 +350,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   using Tile = typename C::Tile;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
+  const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -597,21 +398,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
     const size_t sb = ((size_t)bi * a.H + hh) * a.T + qoff;
     lse2 = buf_ldf(make_rsrc(a.lse2 + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
     dlt = buf_ldf(make_rsrc(a.delta + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      settle(qf[s]);
+      settle(gf[s]);
+    }
+    settle(lse2);
+    settle(dlt);
   }
 
   const Segments seg = fwd_segments(g, a.mode, qh, qt, C::BM, BN);
   const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
   const int ntiles = seg.tiles();
 
-  const RowSeg s0 = make_row_seg<D>(a, g, qh, seg.half0, pw0, pw1, p, sample0, rs, hh, half_bytes);
-  const RowSeg s1 = make_row_seg<D>(a, g, qh, seg.half1, pw0, pw1, p, sample0, rs, hh, half_bytes);
-
-  auto issue_tile = [&](int i, int buf) {
+  ROW_SEGMENTS
+  auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
     const bool second = i >= n0;
     const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    uint16_t* dst = smem + buf * C::BUF;
-    Tile::load(second ? s1.rk : s0.rk, row_bytes, kt * BN, dst, tid);
-    Tile::load(second ? s1.rv : s0.rv, row_bytes, kt * BN, dst + Tile::ELEMS, tid);
+    const size_t kvb = second ? kvb1 : kvb0;
+    const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
+    Tile::load(make_rsrc(a.k + kvb, half_bytes), row_bytes, kt * BN, dst, tid);
+    Tile::load(make_rsrc(a.v + kvb, half_bytes), row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
   };
 
   floatx16 dq[C::DB];
@@ -630,21 +437,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
 
     if (wave_active) {
       const bool second = i >= n0;
-      const RowSeg& sg = second ? s1 : s0;
       const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
-      const int lf = sg.lo_f, hf = sg.hi_f, ll = sg.lo_l, hl = sg.hi_l;
-      const int lo = sg.lo_p, hi = sg.hi_p;
+      const int lf = second ? lo_f1 : lo_f0, hf = second ? hi_f1 : hi_f0;
+      const int ll = second ? lo_l1 : lo_l0, hl = second ? hi_l1 : hi_l0;
+      const int lo = second ? lo_p1 : lo_p0, hi = second ? hi_p1 : hi_p0;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int c0 = k0 + 32 * kb;
         if (c0 >= hl || c0 + 32 <= lf) continue;
         const bool full = ll <= c0 && c0 + 32 <= hf;
         floatx16 sp = zero16(), dp = zero16();
+        mfma_burst_begin();
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
           sp = mfma32(lds_row8<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], sp);
           dp = mfma32(lds_row8<D>(Vs, 32 * kb + l32, 2 * s + h2), gf[s], dp);
         }
+        mfma_burst_end();
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
@@ -654,13 +463,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           }
           dp[r] = pr * (dp[r] - dlt);
         }
+        const bf16x8 sb0 = pack_bf16x8(dp, 0), sb1 = pack_bf16x8(dp, 8);
+        mfma_burst_begin();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 sb = pack_bf16x8(dp, 8 * ks);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            dq[db] = mfma32(lds_trA<D>(Ks, 32 * kb + 16 * ks, 32 * db, lane), sb, dq[db]);
+            dq[db] = mfma32(lds_trA<D>(Ks, 32 * kb + 16 * ks, 32 * db, lane), ks ? sb1 : sb0, dq[db]);
         }
+        mfma_burst_end();
       }
     }
 
@@ -690,17 +501,10 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(256), 0, s, a, rows);
   } else if (stage == 1) {
-#ifdef BDATTN_DKDV_FUSED
-    using KC = DkdvCfg<D>;
-    const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
-    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
-#else
     using KC = DkdvPairCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
     const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
     hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
-#endif
   } else {
     using QC = DqCfg<D>;
     const int qtiles = (a.n + QC::BM - 1) / QC::BM;

@@ -33,11 +33,14 @@
 #include "kernels.h"
 #include "tile_io.h"
 
+#include <type_traits>
+
 namespace bd {
 
-template <int D, int BN>
+template <int D, int BN, int NW_ = 4, int NBUF_ = 2>
 struct FwdCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;      // waves per workgroup (32 query rows each)
+  static constexpr int NBUF = NBUF_;  // depth of the K/V ring in LDS
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
   static constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
@@ -53,33 +56,12 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half) {
   return (a.mode == MODE_DIFFUSION && half == CLEAN) ? a.n : 0;
 }
 
-// What a query-stationary wave needs about one key half: the visible
-// intervals of its first and last rows (block classification), of this
-// lane's row (element mask), and the K / V resources of that half.
-struct RowSeg {
-  int lo_f, hi_f, lo_l, hi_l, lo_p, hi_p;
-  rsrc_t rk, rv;
-};
-
-template <int D>
-__device__ __forceinline__ RowSeg make_row_seg(const AttnArgs& a, const Geom& g, int qh, int kh, int pw0,
-                                               int pw1, int p, size_t sample0, size_t rs, int hh,
-                                               uint32_t half_bytes) {
-  RowSeg s;
-  row_interval(g, qh, kh, pw0, s.lo_f, s.hi_f);
-  row_interval(g, qh, kh, max(pw1 - 1, pw0), s.lo_l, s.hi_l);
-  row_interval(g, qh, kh, p, s.lo_p, s.hi_p);
-  const size_t base = (sample0 + half_offset(a, kh)) * rs + (size_t)hh * D;
-  s.rk = make_rsrc(a.k + base, half_bytes);
-  s.rv = make_rsrc(a.v + base, half_bytes);
-  return s;
-}
-
-template <int D, int BN>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
-  using C = FwdCfg<D, BN>;
+template <int D, int BN, int NW, int NBUF>
+__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
+  using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
+  const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,6 +109,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
       v ^= flip;
       qf[s] = as_bf16x8(v);
     }
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) settle(qf[s]);
   }
   const float cs = fabsf(a.scale) * kLog2e;
 
@@ -134,17 +118,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
   const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
   const int ntiles = seg.tiles();
 
-  // Per segment: the wave's first/last row intervals (block classification),
-  // this lane's interval (element mask) and the K/V resources.
-  const RowSeg s0 = make_row_seg<D>(a, g, qh, seg.half0, pw0, pw1, p, sample0, rs, hh, half_bytes);
-  const RowSeg s1 = make_row_seg<D>(a, g, qh, seg.half1, pw0, pw1, p, sample0, rs, hh, half_bytes);
+  // Per segment (key half): the visible intervals of the wave's first and
+  // last rows (block classification), of this lane's row (element mask),
+  // and row 0 of K / V in that half.  Kept as separate scalars and picked
+  // with selects: grouping them in a struct lets the compiler select
+  // between the structs' addresses, which puts both in scratch memory.
+  int lo_f0, hi_f0, lo_l0, hi_l0, lo_p0, hi_p0, lo_f1, hi_f1, lo_l1, hi_l1, lo_p1, hi_p1;
+  row_interval(g, qh, seg.half0, pw0, lo_f0, hi_f0);
+  row_interval(g, qh, seg.half0, max(pw1 - 1, pw0), lo_l0, hi_l0);
+  row_interval(g, qh, seg.half0, p, lo_p0, hi_p0);
+  row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);
+  row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);
+  row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);
+  const size_t kvb0 = (sample0 + half_offset(a, seg.half0)) * rs + (size_t)hh * D;
+  const size_t kvb1 = (sample0 + half_offset(a, seg.half1)) * rs + (size_t)hh * D;
 
-  auto issue_tile = [&](int i, int buf) {
+  auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
     const bool second = i >= n0;
     const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    uint16_t* dst = smem + buf * C::BUF;
-    Tile::load(second ? s1.rk : s0.rk, row_bytes, kt * BN, dst, tid);
-    Tile::load(second ? s1.rv : s0.rv, row_bytes, kt * BN, dst + Tile::ELEMS, tid);
+    const size_t kvb = second ? kvb1 : kvb0;
+    const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
+    Tile::load(make_rsrc(a.k + kvb, half_bytes), row_bytes, kt * BN, dst, tid);
+    Tile::load(make_rsrc(a.v + kvb, half_bytes), row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
   };
 
   floatx16 o[C::DB];
@@ -153,22 +148,39 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
   float m_run = -INFINITY;  // running maximum, base-2 units, scale applied
   float l_run = 0.f;        // this lane's share of the denominator
 
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_vmem();
+  // Per-lane parts of the LDS addresses, fixed for the whole walk.
+  int koff[C::KS];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) koff[s] = row8_lane_off<D>(lane, 2 * s);
+  int voff[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) voff[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+
+  // Prologue: the first NBUF - 1 tiles in flight, the first one landed.
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ntiles) issue_tile(j, j);
+  wait_tiles<NBUF - 2, Tile::PER>(ntiles > NBUF - 2 ? NBUF - 2 : ntiles - 1);
   __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
-    const bool more = i + 1 < ntiles;
-    if (more) issue_tile(i + 1, (i + 1) & 1);
-    const uint16_t* Ks = smem + (i & 1) * C::BUF;
+  // One tile; BUF (the LDS buffer holding it) is a compile-time constant so
+  // that every LDS read below is a lane register plus an immediate offset.
+  auto tile = [&](auto bufc, int i) __attribute__((always_inline)) {
+    constexpr int BUFI = decltype(bufc)::value;
+    // refill the buffer read in the previous iteration, NBUF - 1 tiles ahead
+    const int ahead = i + NBUF - 1;
+    if (ahead < ntiles) issue_tile(ahead, (BUFI + NBUF - 1) % NBUF);
+    const uint16_t* Ks = smem + BUFI * C::BUF;
     const uint16_t* Vs = Ks + Tile::ELEMS;
 
     if (wave_active) {
       const bool second = i >= n0;
-      const RowSeg& sg = second ? s1 : s0;
       const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
-      const int lf = sg.lo_f, hf = sg.hi_f, ll = sg.lo_l, hl = sg.hi_l;
-      const int lo = sg.lo_p, hi = sg.hi_p;
+      const int lf = second ? lo_f1 : lo_f0, hf = second ? hi_f1 : hi_f0;
+      const int ll = second ? lo_l1 : lo_l0, hl = second ? hi_l1 : hi_l0;
+      const int lo = second ? lo_p1 : lo_p0, hi = second ? hi_p1 : hi_p0;
       int cls[C::KB];
       floatx16 sc[C::KB];
       float mt = -INFINITY;
@@ -180,8 +192,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
                                                 : TILE_PARTIAL;
         if (cls[kb] == TILE_SKIP) continue;
         floatx16 acc = zero16();
+        mfma_burst_begin();
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_row8<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], acc);
+        for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_vec_at(Ks + 32 * kb * D + koff[s]), qf[s], acc);
+        mfma_burst_end();
         if (cls[kb] == TILE_PARTIAL) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -218,18 +232,31 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
           sc[kb][r] = pr;
           l_run += pr;
         }
+        const bf16x8 pb0 = pack_bf16x8(sc[kb], 0), pb1 = pack_bf16x8(sc[kb], 8);
+        mfma_burst_begin();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = pack_bf16x8(sc[kb], 8 * ks);
+          const uint16_t* vrow = Vs + (32 * kb + 16 * ks) * D;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            o[db] = mfma32(lds_trA<D>(Vs, 32 * kb + 16 * ks, 32 * db, lane), pb, o[db]);
+            o[db] = mfma32(lds_trA_at(vrow + voff[db][0], vrow + voff[db][1]), ks ? pb1 : pb0, o[db]);
         }
+        mfma_burst_end();
       }
     }
 
-    wait_vmem();
+    // tile i + 1 must have landed; later ones may stay in flight
+    const int in_flight = min(ntiles - 1, i + NBUF - 1) - (i + 1);
+    wait_tiles<NBUF - 2, Tile::PER>(in_flight);
     __syncthreads();
+  };
+
+  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three tiles");
+  for (int i = 0; i < ntiles; i += NBUF) {
+    tile(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < ntiles) tile(std::integral_constant<int, 1>{}, i + 1);
+    if constexpr (NBUF == 3)
+      if (i + 2 < ntiles) tile(std::integral_constant<int, 2 % NBUF>{}, i + 2);
   }
 
   // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2.
@@ -251,18 +278,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a, int qtiles) {
   }
 }
 
-template <int D, int BN>
+template <int D, int BN, int NW = 4, int NBUF = 2>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
-  using C = FwdCfg<D, BN>;
+  using C = FwdCfg<D, BN, NW, NBUF>;
   const int qtiles = (a.n + C::BM - 1) / C::BM;
   const long long blocks = (long long)qtiles * a.nhalves * a.B * a.H;
-  hipLaunchKernelGGL((fwd_kernel<D, BN>), dim3((unsigned)blocks), dim3(C::NT), 0, s, a, qtiles);
+  hipLaunchKernelGGL((fwd_kernel<D, BN, NW, NBUF>), dim3((unsigned)blocks), dim3(C::NT), 0, s, a, qtiles);
   return hipGetLastError();
 }
 
+#ifndef BDATTN_FWD_NW
+#define BDATTN_FWD_NW 4
+#endif
+#ifndef BDATTN_FWD_NBUF
+#define BDATTN_FWD_NBUF 2
+#endif
+
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
-  if (D == 64) return launch_fwd_t<64, 64>(a, s);
-  return launch_fwd_t<128, 64>(a, s);
+  if (D == 64) return launch_fwd_t<64, 64, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  return launch_fwd_t<128, 64, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }
 
 }  // namespace bd

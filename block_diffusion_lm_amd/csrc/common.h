@@ -71,6 +71,19 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Issue priority of the wave around a burst of MFMAs.  A wave's own vector
+// ALU work does not overlap its MFMAs (measured on MI355X), so throughput
+// comes from the other wave on the SIMD running its softmax arithmetic
+// meanwhile; raising the priority of the wave that is in an MFMA burst keeps
+// the matrix core fed while the other wave fills the remaining issue slots.
+#ifdef BDATTN_SETPRIO
+__device__ __forceinline__ void mfma_burst_begin() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_burst_end() { __builtin_amdgcn_s_setprio(0); }
+#else
+__device__ __forceinline__ void mfma_burst_begin() {}
+__device__ __forceinline__ void mfma_burst_end() {}
+#endif
+
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zeros (the hardware range check), which is how ragged tiles are padded.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -85,20 +98,69 @@ __device__ __forceinline__ float buf_ldf(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
 
-// 16 bytes per lane from a buffer straight into LDS: the wave's 64 lanes
-// fill 1 KiB starting at lds_wave (which must be the same for the wave).
-__device__ __forceinline__ void lds_direct16(rsrc_t r, uint16_t* lds_wave, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave, 16, voff, soff, 0, 0);
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 4 bytes per lane straight into LDS (256 bytes per wave).
-__device__ __forceinline__ void lds_direct4(rsrc_t r, void* lds_wave, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave, 4, voff, soff, 0, 0);
+// Buffer loads that write LDS directly.  The wave's 64 lanes fill
+// consecutive LDS from lds_wave, the wave's LDS byte address (uniform), 16
+// or 4 bytes per lane.
+//
+// They are issued from inline assembly that sets M0 (the LDS base) itself.
+// The compiler's own form of this load makes every later transposing LDS
+// read (ds_read_b64_tr_b16) wait until all such loads in flight have landed,
+// wherever they write, which would stall each tile's products on the load
+// of the next tile.  The kernels order these loads explicitly instead: an
+// LDS buffer is read only after wait_vmem() and a workgroup barrier, and
+// refilled only after the barrier that follows its last reads.  No other
+// code in these kernels keeps a value in M0.
+__device__ __forceinline__ void lds_direct16(rsrc_t r, uint32_t lds_wave, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds_wave)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_direct4(rsrc_t r, uint32_t lds_wave, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds_wave)
+      : "memory");
+}
+
+// Makes the compiler complete a register load here rather than at the
+// register's first use.  When that use sits inside a tile loop the wait it
+// places there also covers the loads into LDS issued in the loop (the
+// counter is shared), which would stall every iteration on the next tile.
+template <typename T>
+__device__ __forceinline__ void settle(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
 // Wait until this wave's loads into LDS (and all its other vector memory
 // loads) have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most `keep` tiles of this wave's tile loads (PER load
+// instructions each, issued in tile order) are still in flight: the oldest
+// tiles have landed.  keep is uniform, 0 <= keep <= MAXKEEP.
+template <int MAXKEEP, int PER>
+__device__ __forceinline__ void wait_tiles(int keep) {
+  if constexpr (MAXKEEP >= 2) {
+    if (keep >= 2) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); return; }
+  }
+  if constexpr (MAXKEEP >= 1) {
+    if (keep >= 1) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); return; }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // 16-byte global load / store helpers (bf16 stored as raw 16-bit words).
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -63,6 +63,35 @@ __device__ __forceinline__ bf16x8 lds_trA(const uint16_t* t, int rbase, int col_
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same two reads with the lane's part of the address precomputed: the
+// kernels keep these per-lane offsets (elements) in registers for the whole
+// walk, so that inside the loops every read is a register plus a
+// compile-time offset (whole 16-row steps leave swz unchanged).
+template <int D>
+__device__ __forceinline__ int row8_lane_off(int lane, int chunk_base) {
+  return nat_off<D>(lane & 31, chunk_base + (lane >> 5));
+}
+
+template <int D>
+__device__ __forceinline__ int trA_lane_off(int lane, int col_base, int upper) {
+  const int l32 = lane & 31, h2 = lane >> 5, s = lane & 15;
+  const int row = 8 * upper + 4 * h2 + (s >> 2);
+  const int col = col_base + (l32 & 16) + 4 * (s & 3);
+  return nat_off<D>(row, col >> 3) + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_vec_at(const uint16_t* p) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 lds_trA_at(const uint16_t* lo, const uint16_t* hi) {
+  bf16x4 a = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                            (__attribute__((address_space(3))) shortx4*)(lo)));
+  bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                            (__attribute__((address_space(3))) shortx4*)(hi)));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Copy rows [row0, row0 + ROWS) of a [n][D] view (row stride row_bytes) into
 // an LDS tile, NT threads cooperating; each lane writes 16 bytes and every
 // wave-wide instruction fills 1 KiB of consecutive LDS.
@@ -74,7 +103,8 @@ struct DirectTile {
   static constexpr int ELEMS = ROWS * D;
   static_assert(SLOTS % NT == 0, "tile must split evenly over the threads");
 
-  __device__ __forceinline__ static void load(rsrc_t src, uint32_t row_bytes, int row0, uint16_t* lds,
+  // lds: LDS byte address of the tile (lds_byte_addr)
+  __device__ __forceinline__ static void load(rsrc_t src, uint32_t row_bytes, int row0, uint32_t lds,
                                               int tid) {
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
@@ -83,7 +113,7 @@ struct DirectTile {
       const int r = slot / CH;
       const int c = (slot % CH) ^ swz<D>(r);
       const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
-      lds_direct16(src, lds + (i * NT + wbase) * 8, voff, (uint32_t)row0 * row_bytes);
+      lds_direct16(src, lds + (uint32_t)(i * NT + wbase) * 16u, voff, (uint32_t)row0 * row_bytes);
     }
   }
 };
