@@ -246,25 +246,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
       for (int s = 0; s < C::KS; ++s) t = mfma32(lds_row8<D>(X, 32 * qb + l32, 2 * s + h2), xf[s], t);
       mfma_burst_end();
       if (pwave) {
-        // P = exp2(S * scale * log2 e - LSE * log2 e), masked off the visible rows
-        float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
+        // P = exp2(S * scale * log2 e - LSE * log2 e)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int rl_ = 32 * qb + 8 * gq + 4 * h2;
-          const float4 l4 = *reinterpret_cast<const float4*>(Ls + rl_);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * gq + j;
-            float pr = fast_exp2(__builtin_fmaf(t[r], a.scale_log2, -lv[j]));
-            if (!full[qb]) {
-              const int row = qt * C::BQ + rl_ + j;
-              pr = (row >= clo && row < chi) ? pr : 0.f;
-            }
-            t[r] = pr;
-          }
-          px[gq * 64] = make_float4(t[4 * gq], t[4 * gq + 1], t[4 * gq + 2], t[4 * gq + 3]);
+          const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
+          t[4 * gq + 0] = fast_exp2(__builtin_fmaf(t[4 * gq + 0], a.scale_log2, -l4.x));
+          t[4 * gq + 1] = fast_exp2(__builtin_fmaf(t[4 * gq + 1], a.scale_log2, -l4.y));
+          t[4 * gq + 2] = fast_exp2(__builtin_fmaf(t[4 * gq + 2], a.scale_log2, -l4.z));
+          t[4 * gq + 3] = fast_exp2(__builtin_fmaf(t[4 * gq + 3], a.scale_log2, -l4.w));
         }
+        if (!full[qb]) {
+          // zero the rows that do not see this lane's key: register r holds
+          // row r0 + 8 (r / 4) + r % 4, r0 = the block's first row + 4 h2
+          const int r0 = qt * C::BQ + 32 * qb + 4 * h2;
+          const int lo = clo - r0, hi = chi - r0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            t[r] = (off >= lo && off < hi) ? t[r] : 0.f;
+          }
+        }
+        float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          px[gq * 64] = make_float4(t[4 * gq], t[4 * gq + 1], t[4 * gq + 2], t[4 * gq + 3]);
         pb[qb][0] = pack_bf16x8(t, 0);
         pb[qb][1] = pack_bf16x8(t, 8);
       } else {
