@@ -9,7 +9,7 @@
 #include <cstdint>
 #include <limits>
 
-#include "../../include/bdattn.h"
+#include "bdattn.h"
 #include "geometry.h"
 #include "kernels.h"
 

@@ -34,6 +34,8 @@
 #include "kernels.h"
 #include "tile_io.h"
 
+#include <type_traits>
+
 namespace bd {
 
 __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
@@ -108,10 +110,19 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long lo
   const size_t kvb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh * D;
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-stationary.
+// dK / dV: key-stationary, one workgroup per 128 keys, 8 waves in 4 pairs.
+// The pair's two waves share 32 keys: the P-wave holds K and computes
+// S = Q K^T, P and dV^T += dO^T P; the dS-wave holds V and computes
+// dP = dO V^T, dS = P (dP - delta) and dK^T += Q^T dS.  The dS-wave needs the
+// P-wave's probabilities, so it runs one query tile behind: in step j the
+// P-wave works on tile j and publishes its P (bf16) in LDS, while the
+// dS-wave works on tile j - 1 with the P published in step j - 1.  One
+// workgroup barrier per step orders everything: the Q / dO ring holds the
+// P-waves' tile, the dS-waves' tile and the tile in flight, and the P
+// exchange is double-buffered.
 // ---------------------------------------------------------------------------
 template <int D>
-struct DkdvPairCfg {
+struct DkdvCfg {
   static constexpr int NPAIR = 4;
   static constexpr int NT = 128 * NPAIR;  // 8 waves
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
@@ -119,19 +130,20 @@ struct DkdvPairCfg {
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
+  static constexpr int NBUF = 3;          // Q / dO ring depth
   using Tile = DirectTile<BQ, D, NT>;
   static constexpr int BUF = 2 * Tile::ELEMS;   // Q then dO
   static constexpr int FBUF = 2 * BQ;           // lse2 then delta
-  static constexpr int PX = NPAIR * QB * 4 * 64;  // float4 slots of the P exchange
+  static constexpr int PXS = NPAIR * QB * 2 * 64;  // 16-byte slots of one P exchange buffer
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int ktiles) {
-  using C = DkdvPairCfg<D>;
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
+  using C = DkdvCfg<D>;
   using Tile = typename C::Tile;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::BUF];
-  __shared__ __attribute__((aligned(16))) float fsm[2 * C::FBUF];
-  __shared__ __attribute__((aligned(16))) float4 pex[C::PX];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NBUF * C::BUF];
+  __shared__ __attribute__((aligned(16))) float fsm[C::NBUF * C::FBUF];
+  __shared__ __attribute__((aligned(16))) u32x4 pex[2 * C::PXS];
   const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(smem));
   const uint32_t fbase = __builtin_amdgcn_readfirstlane(lds_byte_addr(fsm));
 
@@ -195,10 +207,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
     // rows past the half read lse2 = delta = 0; their Q and dO rows are
     // zero too, so they add nothing to dV or dK
     const uint32_t sbytes = (uint32_t)a.n * 4u;
+    const uint32_t fdst = fbase + (uint32_t)(buf * C::FBUF) * 4u;
     if (wv == 0)
-      lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fbase + (uint32_t)(buf * C::FBUF) * 4u, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
+      lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fdst, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
     if (wv == 1)
-      lds_direct4(make_rsrc(a.delta + sb, sbytes), fbase + (uint32_t)(buf * C::FBUF + C::BQ) * 4u, (uint32_t)lane * 4u,
+      lds_direct4(make_rsrc(a.delta + sb, sbytes), fdst + C::BQ * 4u, (uint32_t)lane * 4u,
                   (uint32_t)qt * C::BQ * 4u);
   };
 
@@ -210,111 +223,179 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(AttnArgs a, int k
   wait_vmem();
   __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
-    const bool more = i + 1 < ntiles;
-    if (more) issue_tile(i + 1, (i + 1) & 1);
-    const int buf = i & 1;
-    const uint16_t* Qs = smem + buf * C::BUF;
-    const uint16_t* Ds = Qs + Tile::ELEMS;
-    const float* Ls = fsm + buf * C::FBUF;
-    const float* Dl = Ls + C::BQ;
+  // The two roles run separate copies of the walk, so that each is
+  // register-allocated for its own state only.  Both pass one workgroup
+  // barrier per step, ntiles + 1 steps.
+  auto walk = [&](auto rolec) __attribute__((always_inline)) {
+    constexpr bool PW = decltype(rolec)::value;
+    // Per-lane LDS offsets (elements from the start of a buffer), fixed for
+    // the walk: the first product reads the wave's A operand tile (Q for the
+    // P-wave, dO for the dS-wave) row-wise, the second reads the other tile
+    // transposed.
+    constexpr int xsel = PW ? 0 : Tile::ELEMS;
+    constexpr int ysel = PW ? Tile::ELEMS : 0;
+    int xoff[C::KS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) xoff[s] = xsel + row8_lane_off<D>(lane, 2 * s);
+    int yoff[C::DB][2];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) yoff[db][u] = ysel + trA_lane_off<D>(lane, 32 * db, u);
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    static_assert(C::QB == 2, "two 32-row blocks per query tile");
 
-    const bool second = i >= n0;
-    const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
-    const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
-    const int clo = second ? clo_p1 : clo_p0, chi = second ? chi_p1 : chi_p0;
-    bool act[C::QB], full[C::QB];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int r0 = qt * C::BQ + 32 * qb;
-      const int r1 = min(r0 + 32, a.n);
-      act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
-      full[qb] = r0 >= cl && r1 <= hf;
-    }
+    // ring slots (tile index mod NBUF) of the tile issued in this step and
+    // of this wave's tile
+    int slot_next = 1;
+    int slot = PW ? 0 : C::NBUF - 1;
+    auto advance = [](int x) { return x == C::NBUF - 1 ? 0 : x + 1; };
+    for (int j = 0; j <= ntiles; ++j) {
+      if (j + 1 < ntiles) issue_tile(j + 1, slot_next);
+      const int i = PW ? j : j - 1;  // this wave's tile
+      if (PW ? (j < ntiles) : (j >= 1)) {
+        const uint16_t* Tb = smem + slot * C::BUF;
+        const float* Ls = fsm + slot * C::FBUF;
+        const float* Dl = Ls + C::BQ;
+        u32x4* px = pex + (i & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
 
-    // Phase 1: S and P (P-wave, which publishes P), dP (dS-wave).
-    bf16x8 pb[C::QB][2];
-    floatx16 dp[C::QB];
+        const bool second = i >= n0;
+        const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+        const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
+        const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
+        const int clo = second ? clo_p1 : clo_p0, chi = second ? chi_p1 : chi_p0;
+        bool act[C::QB], full[C::QB];
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      if (!act[qb]) continue;
-      const uint16_t* X = pwave ? Qs : Ds;
-      floatx16 t = zero16();
-      mfma_burst_begin();
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) t = mfma32(lds_row8<D>(X, 32 * qb + l32, 2 * s + h2), xf[s], t);
-      mfma_burst_end();
-      if (pwave) {
-        // P = exp2(S * scale * log2 e - LSE * log2 e)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
-          t[4 * gq + 0] = fast_exp2(__builtin_fmaf(t[4 * gq + 0], a.scale_log2, -l4.x));
-          t[4 * gq + 1] = fast_exp2(__builtin_fmaf(t[4 * gq + 1], a.scale_log2, -l4.y));
-          t[4 * gq + 2] = fast_exp2(__builtin_fmaf(t[4 * gq + 2], a.scale_log2, -l4.z));
-          t[4 * gq + 3] = fast_exp2(__builtin_fmaf(t[4 * gq + 3], a.scale_log2, -l4.w));
+        for (int qb = 0; qb < C::QB; ++qb) {
+          const int r0 = qt * C::BQ + 32 * qb;
+          const int r1 = min(r0 + 32, a.n);
+          act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
+          full[qb] = r0 >= cl && r1 <= hf;
         }
-        if (!full[qb]) {
-          // zero the rows that do not see this lane's key: register r holds
-          // row r0 + 8 (r / 4) + r % 4, r0 = the block's first row + 4 h2
-          const int r0 = qt * C::BQ + 32 * qb + 4 * h2;
-          const int lo = clo - r0, hi = chi - r0;
+
+        // First product of one or both 32-row blocks: S^T (P-wave) or dP^T
+        // (dS-wave), one key per lane.  With both blocks the two chains are
+        // interleaved and the operand reads run PF steps ahead of the
+        // products, an order pinned with scheduling barriers (left alone,
+        // the scheduler keeps two reads in flight and every product waits
+        // for its read).
+        floatx16 t[C::QB];
+        auto product1_both = [&]() __attribute__((always_inline)) {
+          constexpr int PF = 2;
+          t[0] = zero16();
+          t[1] = zero16();
+          bf16x8 a0[C::KS], a1[C::KS];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);
-            t[r] = (off >= lo && off < hi) ? t[r] : 0.f;
+          for (int s = 0; s < PF; ++s) {
+            a0[s] = lds_vec_at(Tb + xoff[s]);
+            a1[s] = lds_vec_at(Tb + 32 * D + xoff[s]);
           }
+#pragma unroll
+          for (int s = 0; s < C::KS; ++s) {
+            if (s + PF < C::KS) {
+              a0[s + PF] = lds_vec_at(Tb + xoff[s + PF]);
+              a1[s + PF] = lds_vec_at(Tb + 32 * D + xoff[s + PF]);
+            }
+            t[0] = mfma32(a0[s], xf[s], t[0]);
+            t[1] = mfma32(a1[s], xf[s], t[1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        auto product1 = [&](auto qbc) __attribute__((always_inline)) {
+          constexpr int qb = decltype(qbc)::value;
+          t[qb] = zero16();
+#pragma unroll
+          for (int s = 0; s < C::KS; ++s) t[qb] = mfma32(lds_vec_at(Tb + 32 * qb * D + xoff[s]), xf[s], t[qb]);
+        };
+        // B operand of the second product, two 16-row halves of the block
+        bf16x8 bop[C::QB][2];
+        auto operand2 = [&](auto qbc) __attribute__((always_inline)) {
+          constexpr int qb = decltype(qbc)::value;
+          floatx16& x = t[qb];
+          if constexpr (PW) {
+            // P = exp2(S * scale * log2 e - LSE * log2 e)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
+              x[4 * gq + 0] = fast_exp2(__builtin_fmaf(x[4 * gq + 0], a.scale_log2, -l4.x));
+              x[4 * gq + 1] = fast_exp2(__builtin_fmaf(x[4 * gq + 1], a.scale_log2, -l4.y));
+              x[4 * gq + 2] = fast_exp2(__builtin_fmaf(x[4 * gq + 2], a.scale_log2, -l4.z));
+              x[4 * gq + 3] = fast_exp2(__builtin_fmaf(x[4 * gq + 3], a.scale_log2, -l4.w));
+            }
+            if (!full[qb]) {
+              // zero the rows that do not see this lane's key: register r
+              // holds row r0 + 8 (r / 4) + r % 4, r0 = first row + 4 h2
+              const int r0 = qt * C::BQ + 32 * qb + 4 * h2;
+              const int lo = clo - r0, hi = chi - r0;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                x[r] = (off >= lo && off < hi) ? x[r] : 0.f;
+              }
+            }
+            bop[qb][0] = pack_bf16x8(x, 0);
+            bop[qb][1] = pack_bf16x8(x, 8);
+            // publish P for the dS-wave of the pair (read in the next step)
+            px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, bop[qb][0]);
+            px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, bop[qb][1]);
+          } else {
+            // dS = P (dP - delta), P as published by the P-wave (bf16)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const u32x4 pw = px[(qb * 2 + u) * 64];
+#pragma unroll
+              for (int gq = 0; gq < 2; ++gq) {
+                const float4 d4 = *reinterpret_cast<const float4*>(Dl + 32 * qb + 8 * (2 * u + gq) + 4 * h2);
+                const int r = 8 * u + 4 * gq;
+                const uint32_t w0 = pw[2 * gq], w1 = pw[2 * gq + 1];
+                x[r + 0] = __builtin_bit_cast(float, w0 << 16) * (x[r + 0] - d4.x);
+                x[r + 1] = __builtin_bit_cast(float, w0 & 0xffff0000u) * (x[r + 1] - d4.y);
+                x[r + 2] = __builtin_bit_cast(float, w1 << 16) * (x[r + 2] - d4.z);
+                x[r + 3] = __builtin_bit_cast(float, w1 & 0xffff0000u) * (x[r + 3] - d4.w);
+              }
+            }
+            bop[qb][0] = pack_bf16x8(x, 0);
+            bop[qb][1] = pack_bf16x8(x, 8);
+          }
+        };
+        // dV^T += dO^T P (P-wave), dK^T += Q^T dS (dS-wave)
+        auto product2 = [&](auto qbc) __attribute__((always_inline)) {
+          constexpr int qb = decltype(qbc)::value;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint16_t* yr = Tb + (32 * qb + 16 * ks) * D;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+              acc[db] = mfma32(lds_trA_at(yr + yoff[db][0], yr + yoff[db][1]), bop[qb][ks], acc[db]);
+          }
+        };
+        if (act[0] && act[1]) {
+          product1_both();
+          operand2(Q0{});
+          operand2(Q1{});
+          product2(Q0{});
+          product2(Q1{});
+        } else if (act[0]) {
+          product1(Q0{});
+          operand2(Q0{});
+          product2(Q0{});
+        } else if (act[1]) {
+          product1(Q1{});
+          operand2(Q1{});
+          product2(Q1{});
         }
-        float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          px[gq * 64] = make_float4(t[4 * gq], t[4 * gq + 1], t[4 * gq + 2], t[4 * gq + 3]);
-        pb[qb][0] = pack_bf16x8(t, 0);
-        pb[qb][1] = pack_bf16x8(t, 8);
-      } else {
-        dp[qb] = t;
       }
+      wait_vmem();
+      __syncthreads();
+      slot_next = advance(slot_next);
+      slot = advance(slot);
     }
-    __syncthreads();
-
-    // Phase 2: dV^T += dO^T P (P-wave); dS = P (dP - delta), dK^T += Q^T dS (dS-wave).
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      if (!act[qb]) continue;
-      bf16x8 bop[2];
-      if (pwave) {
-        bop[0] = pb[qb][0];
-        bop[1] = pb[qb][1];
-      } else {
-        const float4* px = pex + (pair * C::QB + qb) * 4 * 64 + lane;
-        floatx16 t = dp[qb];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int rl_ = 32 * qb + 8 * gq + 4 * h2;
-          const float4 d4 = *reinterpret_cast<const float4*>(Dl + rl_);
-          const float4 p4 = px[gq * 64];
-          t[4 * gq + 0] = p4.x * (t[4 * gq + 0] - d4.x);
-          t[4 * gq + 1] = p4.y * (t[4 * gq + 1] - d4.y);
-          t[4 * gq + 2] = p4.z * (t[4 * gq + 2] - d4.z);
-          t[4 * gq + 3] = p4.w * (t[4 * gq + 3] - d4.w);
-        }
-        bop[0] = pack_bf16x8(t, 0);
-        bop[1] = pack_bf16x8(t, 8);
-      }
-      const uint16_t* Y = pwave ? Ds : Qs;
-      mfma_burst_begin();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = mfma32(lds_trA<D>(Y, 32 * qb + 16 * ks, 32 * db, lane), bop[ks], acc[db]);
-      mfma_burst_end();
-    }
-
-    wait_vmem();
-    __syncthreads();
-  }
+  };
+  if (pwave)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 
   // lane = key, register r of block db = dimension 32db + 8(r/4) + 4h2 + r%4
   if (pair_active && key < a.n) {
@@ -506,10 +587,10 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(256), 0, s, a, rows);
   } else if (stage == 1) {
-    using KC = DkdvPairCfg<D>;
+    using KC = DkdvCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
     const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
   } else {
     using QC = DqCfg<D>;
     const int qtiles = (a.n + QC::BM - 1) / QC::BM;
