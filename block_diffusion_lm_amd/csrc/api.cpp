@@ -99,8 +99,8 @@ int bwd_common(int mode, int stage, const void* q, const void* k, const void* v,
   a.o = static_cast<const uint16_t*>(out);
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse_in = lse;
-  a.delta = static_cast<float*>(workspace);
-  a.lse2 = a.delta + (size_t)B * H * T;
+  a.ndelta = static_cast<float*>(workspace);
+  a.lse2 = a.ndelta + (size_t)B * H * T;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);

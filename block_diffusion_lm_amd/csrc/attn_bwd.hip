@@ -1,6 +1,6 @@
 // attn_bwd.hip -- backward pass, split in three kernels:
 //
-//   preprocess : per query row, delta_i = dO_i . O_i and lse_i * log2(e)
+//   preprocess : per query row, -delta_i = -(dO_i . O_i) and lse_i * log2(e)
 //                (both float32, into the caller's workspace);
 //   dkdv       : one workgroup per 128-key tile; it walks the query tiles
 //                that see its keys and accumulates dV = P^T dO and
@@ -43,7 +43,7 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
 }
 
 // ---------------------------------------------------------------------------
-// delta_i = sum_d dO[i][d] * O[i][d] and lse2_i = lse_i * log2(e); one
+// -delta_i = -sum_d dO[i][d] * O[i][d] and lse2_i = lse_i * log2(e); one
 // 16-byte chunk per lane, rows of D / 8 lanes reduced with shuffles.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long lo
     const long long t = bt % a.T;
     const long long b = bt / a.T;
     const long long si = (b * a.H + h) * a.T + t;
-    a.delta[si] = acc;
+    a.ndelta[si] = -acc;
     a.lse2[si] = a.lse_in[si] * kLog2e;
   }
 }
@@ -133,7 +133,7 @@ struct DkdvCfg {
   static constexpr int NBUF = 3;          // Q / dO ring depth
   using Tile = DirectTile<BQ, D, NT>;
   static constexpr int BUF = 2 * Tile::ELEMS;   // Q then dO
-  static constexpr int FBUF = 2 * BQ;           // lse2 then delta
+  static constexpr int FBUF = 2 * BQ;           // lse2 then -delta
   static constexpr int PXS = NPAIR * QB * 2 * 64;  // 16-byte slots of one P exchange buffer
 };
 
@@ -204,14 +204,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
     Tile::load(make_rsrc(a.q + qb, half_bytes), row_bytes, qt * C::BQ, dst, tid);
     Tile::load(make_rsrc(a.dout + qb, half_bytes), row_bytes, qt * C::BQ, dst + Tile::ELEMS * 2u, tid);
-    // rows past the half read lse2 = delta = 0; their Q and dO rows are
+    // rows past the half read lse2 = -delta = 0; their Q and dO rows are
     // zero too, so they add nothing to dV or dK
     const uint32_t sbytes = (uint32_t)a.n * 4u;
     const uint32_t fdst = fbase + (uint32_t)(buf * C::FBUF) * 4u;
     if (wv == 0)
       lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fdst, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
     if (wv == 1)
-      lds_direct4(make_rsrc(a.delta + sb, sbytes), fdst + C::BQ * 4u, (uint32_t)lane * 4u,
+      lds_direct4(make_rsrc(a.ndelta + sb, sbytes), fdst + C::BQ * 4u, (uint32_t)lane * 4u,
                   (uint32_t)qt * C::BQ * 4u);
   };
 
@@ -225,7 +225,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 
   // The two roles run separate copies of the walk, so that each is
   // register-allocated for its own state only.  Both pass one workgroup
-  // barrier per step, ntiles + 1 steps.
+  // barrier per step, ntiles + 1 steps.  In step j the P-wave computes S, P
+  // and dV for tile j (products, elementwise, products); the dS-wave first
+  // finishes tile j - 1 (dS from the dP it computed in the previous step,
+  // then dK) and then computes dP for tile j.  The two waves of a pair share
+  // a SIMD, and this order puts one wave's elementwise work beside the
+  // other's products.
   auto walk = [&](auto rolec) __attribute__((always_inline)) {
     constexpr bool PW = decltype(rolec)::value;
     // Per-lane LDS offsets (elements from the start of a buffer), fixed for
@@ -246,75 +251,106 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     using Q1 = std::integral_constant<int, 1>;
     static_assert(C::QB == 2, "two 32-row blocks per query tile");
 
-    // ring slots (tile index mod NBUF) of the tile issued in this step and
-    // of this wave's tile
-    int slot_next = 1;
-    int slot = PW ? 0 : C::NBUF - 1;
-    auto advance = [](int x) { return x == C::NBUF - 1 ? 0 : x + 1; };
-    for (int j = 0; j <= ntiles; ++j) {
-      if (j + 1 < ntiles) issue_tile(j + 1, slot_next);
-      const int i = PW ? j : j - 1;  // this wave's tile
-      if (PW ? (j < ntiles) : (j >= 1)) {
-        const uint16_t* Tb = smem + slot * C::BUF;
-        const float* Ls = fsm + slot * C::FBUF;
-        const float* Dl = Ls + C::BQ;
-        u32x4* px = pex + (i & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
+    // Which 32-row blocks of tile i see some key of the pair (act) or every
+    // key of it (full); qt, and the rows [clo, chi) that see this lane's key.
+    auto blocks = [&](int i, bool (&act)[C::QB], bool (&full)[C::QB], int& qt, int& clo, int& chi)
+        __attribute__((always_inline)) {
+      const bool second = i >= n0;
+      qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
+      const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
+      const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
+      clo = second ? clo_p1 : clo_p0;
+      chi = second ? chi_p1 : chi_p0;
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const int r0 = qt * C::BQ + 32 * qb;
+        const int r1 = min(r0 + 32, a.n);
+        act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
+        full[qb] = r0 >= cl && r1 <= hf;
+      }
+    };
 
-        const bool second = i >= n0;
-        const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-        const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
-        const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
-        const int clo = second ? clo_p1 : clo_p0, chi = second ? chi_p1 : chi_p0;
-        bool act[C::QB], full[C::QB];
+    // First product of the active blocks of the tile at Tb: S^T (P-wave)
+    // or dP^T (dS-wave), one key per lane.  With both blocks the two chains
+    // are interleaved and the operand reads run PF steps ahead of the
+    // products, an order pinned with scheduling barriers (left alone, the
+    // scheduler keeps two reads in flight and every product waits for its
+    // read).
+    //
+    // The accumulators start at init(qb): zero for S; for dP the rows'
+    // -delta, so that the chain yields dP - delta.
+    auto product1 = [&](const uint16_t* Tb, const bool (&act)[C::QB], floatx16 (&t)[C::QB], auto init)
+        __attribute__((always_inline)) {
+      if (act[0] && act[1]) {
+        constexpr int PF = 2;
+        t[0] = init(0);
+        t[1] = init(1);
+        bf16x8 a0[C::KS], a1[C::KS];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+          a0[s] = lds_vec_at(Tb + xoff[s]);
+          a1[s] = lds_vec_at(Tb + 32 * D + xoff[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+          if (s + PF < C::KS) {
+            a0[s + PF] = lds_vec_at(Tb + xoff[s + PF]);
+            a1[s + PF] = lds_vec_at(Tb + 32 * D + xoff[s + PF]);
+          }
+          t[0] = mfma32(a0[s], xf[s], t[0]);
+          t[1] = mfma32(a1[s], xf[s], t[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
-          const int r0 = qt * C::BQ + 32 * qb;
-          const int r1 = min(r0 + 32, a.n);
-          act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
-          full[qb] = r0 >= cl && r1 <= hf;
-        }
-
-        // First product of one or both 32-row blocks: S^T (P-wave) or dP^T
-        // (dS-wave), one key per lane.  With both blocks the two chains are
-        // interleaved and the operand reads run PF steps ahead of the
-        // products, an order pinned with scheduling barriers (left alone,
-        // the scheduler keeps two reads in flight and every product waits
-        // for its read).
-        floatx16 t[C::QB];
-        auto product1_both = [&]() __attribute__((always_inline)) {
-          constexpr int PF = 2;
-          t[0] = zero16();
-          t[1] = zero16();
-          bf16x8 a0[C::KS], a1[C::KS];
-#pragma unroll
-          for (int s = 0; s < PF; ++s) {
-            a0[s] = lds_vec_at(Tb + xoff[s]);
-            a1[s] = lds_vec_at(Tb + 32 * D + xoff[s]);
-          }
-#pragma unroll
-          for (int s = 0; s < C::KS; ++s) {
-            if (s + PF < C::KS) {
-              a0[s + PF] = lds_vec_at(Tb + xoff[s + PF]);
-              a1[s + PF] = lds_vec_at(Tb + 32 * D + xoff[s + PF]);
-            }
-            t[0] = mfma32(a0[s], xf[s], t[0]);
-            t[1] = mfma32(a1[s], xf[s], t[1]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        };
-        auto product1 = [&](auto qbc) __attribute__((always_inline)) {
-          constexpr int qb = decltype(qbc)::value;
-          t[qb] = zero16();
+          if (!act[qb]) continue;
+          t[qb] = init(qb);
 #pragma unroll
           for (int s = 0; s < C::KS; ++s) t[qb] = mfma32(lds_vec_at(Tb + 32 * qb * D + xoff[s]), xf[s], t[qb]);
-        };
-        // B operand of the second product, two 16-row halves of the block
-        bf16x8 bop[C::QB][2];
-        auto operand2 = [&](auto qbc) __attribute__((always_inline)) {
-          constexpr int qb = decltype(qbc)::value;
-          floatx16& x = t[qb];
-          if constexpr (PW) {
-            // P = exp2(S * scale * log2 e - LSE * log2 e)
+        }
+      }
+    };
+    // Second product: dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave)
+    // for block qb of the tile at Tb, B operand halves bop.
+    auto product2 = [&](const uint16_t* Tb, auto qbc, const bf16x8 (&bop)[2]) __attribute__((always_inline)) {
+      constexpr int qb = decltype(qbc)::value;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* yr = Tb + (32 * qb + 16 * ks) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = mfma32(lds_trA_at(yr + yoff[db][0], yr + yoff[db][1]), bop[ks], acc[db]);
+      }
+    };
+
+    // ring slots (tile index mod NBUF) of the tile issued in this step and
+    // of tile j
+    int slot_next = 1;
+    int slot = 0;
+    auto advance = [](int x) { return x == C::NBUF - 1 ? 0 : x + 1; };
+    // dS-wave: dP of the previous tile and which of its blocks are active
+    floatx16 dpr[C::QB];
+    bool pact[C::QB] = {false, false};
+    for (int j = 0; j <= ntiles; ++j) {
+      if (j + 1 < ntiles) issue_tile(j + 1, slot_next);
+      const int slot_prev = slot == 0 ? C::NBUF - 1 : slot - 1;
+      if constexpr (PW) {
+        if (j < ntiles) {
+          const uint16_t* Tb = smem + slot * C::BUF;
+          const float* Ls = fsm + slot * C::FBUF;
+          u32x4* px = pex + (j & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
+          bool act[C::QB], full[C::QB];
+          int qt, clo, chi;
+          blocks(j, act, full, qt, clo, chi);
+          floatx16 t[C::QB];
+          product1(Tb, act, t, [](int) { return zero16(); });
+          // P = exp2(S * scale * log2 e - LSE * log2 e), published for the
+          // dS-wave of the pair (read in the next step)
+          auto step = [&](auto qbc) __attribute__((always_inline)) {
+            constexpr int qb = decltype(qbc)::value;
+            if (!act[qb]) return;
+            floatx16& x = t[qb];
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
@@ -334,56 +370,59 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
                 x[r] = (off >= lo && off < hi) ? x[r] : 0.f;
               }
             }
-            bop[qb][0] = pack_bf16x8(x, 0);
-            bop[qb][1] = pack_bf16x8(x, 8);
-            // publish P for the dS-wave of the pair (read in the next step)
-            px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, bop[qb][0]);
-            px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, bop[qb][1]);
-          } else {
-            // dS = P (dP - delta), P as published by the P-wave (bf16)
+            const bf16x8 bop[2] = {pack_bf16x8(x, 0), pack_bf16x8(x, 8)};
+            px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, bop[0]);
+            px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, bop[1]);
+            product2(Tb, qbc, bop);
+          };
+          step(Q0{});
+          step(Q1{});
+        }
+      } else {
+        if (j >= 1) {
+          // dS = P (dP - delta) and dK for tile j - 1, P as published by the
+          // P-wave (bf16); dpr already holds dP - delta
+          const uint16_t* Tb = smem + slot_prev * C::BUF;
+          const u32x4* px = pex + ((j - 1) & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
+          auto step = [&](auto qbc) __attribute__((always_inline)) {
+            constexpr int qb = decltype(qbc)::value;
+            if (!pact[qb]) return;
+            floatx16& x = dpr[qb];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const u32x4 pw = px[(qb * 2 + u) * 64];
 #pragma unroll
-              for (int gq = 0; gq < 2; ++gq) {
-                const float4 d4 = *reinterpret_cast<const float4*>(Dl + 32 * qb + 8 * (2 * u + gq) + 4 * h2);
-                const int r = 8 * u + 4 * gq;
-                const uint32_t w0 = pw[2 * gq], w1 = pw[2 * gq + 1];
-                x[r + 0] = __builtin_bit_cast(float, w0 << 16) * (x[r + 0] - d4.x);
-                x[r + 1] = __builtin_bit_cast(float, w0 & 0xffff0000u) * (x[r + 1] - d4.y);
-                x[r + 2] = __builtin_bit_cast(float, w1 << 16) * (x[r + 2] - d4.z);
-                x[r + 3] = __builtin_bit_cast(float, w1 & 0xffff0000u) * (x[r + 3] - d4.w);
+              for (int w = 0; w < 4; ++w) {
+                x[8 * u + 2 * w] *= __builtin_bit_cast(float, pw[w] << 16);
+                x[8 * u + 2 * w + 1] *= __builtin_bit_cast(float, pw[w] & 0xffff0000u);
               }
             }
-            bop[qb][0] = pack_bf16x8(x, 0);
-            bop[qb][1] = pack_bf16x8(x, 8);
-          }
-        };
-        // dV^T += dO^T P (P-wave), dK^T += Q^T dS (dS-wave)
-        auto product2 = [&](auto qbc) __attribute__((always_inline)) {
-          constexpr int qb = decltype(qbc)::value;
+            const bf16x8 bop[2] = {pack_bf16x8(x, 0), pack_bf16x8(x, 8)};
+            product2(Tb, qbc, bop);
+          };
+          step(Q0{});
+          step(Q1{});
+        }
+        if (j < ntiles) {
+          bool full[C::QB];
+          int qt, clo, chi;
+          blocks(j, pact, full, qt, clo, chi);
+          // register r of block qb holds row 32 qb + 8 (r / 4) + 4 h2 + r % 4
+          const float* Nd = fsm + slot * C::FBUF + C::BQ;
+          product1(smem + slot * C::BUF, pact, dpr, [&](int qb) {
+            floatx16 z;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint16_t* yr = Tb + (32 * qb + 16 * ks) * D;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-              acc[db] = mfma32(lds_trA_at(yr + yoff[db][0], yr + yoff[db][1]), bop[qb][ks], acc[db]);
-          }
-        };
-        if (act[0] && act[1]) {
-          product1_both();
-          operand2(Q0{});
-          operand2(Q1{});
-          product2(Q0{});
-          product2(Q1{});
-        } else if (act[0]) {
-          product1(Q0{});
-          operand2(Q0{});
-          product2(Q0{});
-        } else if (act[1]) {
-          product1(Q1{});
-          operand2(Q1{});
-          product2(Q1{});
+            for (int gq = 0; gq < 4; ++gq) {
+              const float4 d4 = *reinterpret_cast<const float4*>(Nd + 32 * qb + 8 * gq + 4 * h2);
+              z[4 * gq + 0] = d4.x;
+              z[4 * gq + 1] = d4.y;
+              z[4 * gq + 2] = d4.z;
+              z[4 * gq + 3] = d4.w;
+            }
+            return z;
+          });
+        } else {
+          pact[0] = pact[1] = false;
         }
       }
       wait_vmem();
@@ -470,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   // Q and dO as B operands; rows past the half read as zero, and so do their
   // statistics, which makes their dS zero.
   bf16x8 qf[C::KS], gf[C::KS];
-  float lse2, dlt;
+  float lse2, ndlt;
   {
     const size_t qb = (sample0 + qoff) * rs + (size_t)hh * D;
     const rsrc_t rq = make_rsrc(a.q + qb, half_bytes);
@@ -483,14 +522,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
     }
     const size_t sb = ((size_t)bi * a.H + hh) * a.T + qoff;
     lse2 = buf_ldf(make_rsrc(a.lse2 + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
-    dlt = buf_ldf(make_rsrc(a.delta + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+    ndlt = buf_ldf(make_rsrc(a.ndelta + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       settle(qf[s]);
       settle(gf[s]);
     }
     settle(lse2);
-    settle(dlt);
+    settle(ndlt);
   }
 
   const Segments seg = fwd_segments(g, a.mode, qh, qt, C::BM, BN);
@@ -547,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
             const int kk = c0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
             pr = (kk >= lo && kk < hi) ? pr : 0.f;
           }
-          dp[r] = pr * (dp[r] - dlt);
+          dp[r] = pr * (dp[r] + ndlt);
         }
         const bf16x8 sb0 = pack_bf16x8(dp, 0), sb1 = pack_bf16x8(dp, 8);
         mfma_burst_begin();

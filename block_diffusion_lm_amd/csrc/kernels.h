@@ -19,7 +19,7 @@ struct AttnArgs {
   float* lse;            // [B][H][T], natural log
   // backward
   const float* lse_in;   // [B][H][T]
-  float* delta;          // workspace [B][H][T]: dout_i . out_i
+  float* ndelta;         // workspace [B][H][T]: -(dout_i . out_i)
   float* lse2;           // workspace [B][H][T]: lse * log2(e)
   uint16_t* dq;
   uint16_t* dk;
@@ -38,7 +38,7 @@ struct AttnArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, int D, hipStream_t s);
-// One backward kernel: 0 = preprocess (delta), 1 = dK/dV, 2 = dQ.
+// One backward kernel: 0 = preprocess (-delta, lse2), 1 = dK/dV, 2 = dQ.
 hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s);
 
 }  // namespace bd

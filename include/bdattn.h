@@ -73,7 +73,7 @@ int diffusion_attn_fwd(const void* q, const void* k, const void* v, void* out, f
                        int B, int n, int H, int D, int block_size, float scale, void* stream);
 
 /* Bytes of device workspace diffusion_attn_bwd needs: two float32 values
- * per query row ([B][H][2n] each), delta_i = dout_i . out_i and the
+ * per query row ([B][H][2n] each), -delta_i = -(dout_i . out_i) and the
  * log-sum-exp in base 2.  Returns 0 on bad sizes. */
 size_t diffusion_attn_bwd_workspace_size(int B, int n, int H, int D);
 
@@ -101,7 +101,7 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
  * One stage of the backward pass (same arguments as diffusion_attn_bwd /
  * causal_attn_bwd; mode 0 = diffusion with block_size, 1 = causal with n = S
  * and block_size ignored):
- *   stage 0 -- writes the per-row delta_i = dout_i . out_i and lse_i * log2(e)
+ *   stage 0 -- writes the per-row -delta_i = -(dout_i . out_i) and lse_i * log2(e)
  *              to the workspace;
  *   stage 1 -- dK and dV (reads the workspace);
  *   stage 2 -- dQ (reads the workspace).
