@@ -550,14 +550,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) dq[i] = zero16();
 
+  // Per-lane LDS offsets (elements from the start of a buffer): natural rows
+  // of K and V (S^T = K Q^T, dP^T = V dO^T) and transposed K (dQ^T).
+  int roff[C::KS];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) roff[s] = row8_lane_off<D>(lane, 2 * s);
+  int toff[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) toff[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+
   if (ntiles > 0) issue_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
-    const bool more = i + 1 < ntiles;
-    if (more) issue_tile(i + 1, (i + 1) & 1);
-    const uint16_t* Ks = smem + (i & 1) * C::BUF;
+  // One key tile; BUF (the LDS buffer holding it) is a compile-time
+  // constant so that every LDS read is a lane register plus an immediate.
+  auto tile = [&](auto bufc, int i) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (i + 1 < ntiles) issue_tile(i + 1, BUF ^ 1);
+    const uint16_t* Ks = smem + BUF * C::BUF;
     const uint16_t* Vs = Ks + Tile::ELEMS;
 
     if (wave_active) {
@@ -571,37 +584,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
         const int c0 = k0 + 32 * kb;
         if (c0 >= hl || c0 + 32 <= lf) continue;
         const bool full = ll <= c0 && c0 + 32 <= hf;
+        // S^T and dP^T, two interleaved chains with the operand reads PF
+        // products ahead (order pinned with scheduling barriers)
+        constexpr int PF = 2;
         floatx16 sp = zero16(), dp = zero16();
-        mfma_burst_begin();
+        bf16x8 ak[C::KS], av[C::KS];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+          ak[s] = lds_vec_at(Ks + 32 * kb * D + roff[s]);
+          av[s] = lds_vec_at(Vs + 32 * kb * D + roff[s]);
+        }
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-          sp = mfma32(lds_row8<D>(Ks, 32 * kb + l32, 2 * s + h2), qf[s], sp);
-          dp = mfma32(lds_row8<D>(Vs, 32 * kb + l32, 2 * s + h2), gf[s], dp);
-        }
-        mfma_burst_end();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
-          if (!full) {
-            const int kk = c0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            pr = (kk >= lo && kk < hi) ? pr : 0.f;
+          if (s + PF < C::KS) {
+            ak[s + PF] = lds_vec_at(Ks + 32 * kb * D + roff[s + PF]);
+            av[s + PF] = lds_vec_at(Vs + 32 * kb * D + roff[s + PF]);
           }
-          dp[r] = pr * (dp[r] + ndlt);
+          sp = mfma32(ak[s], qf[s], sp);
+          dp = mfma32(av[s], gf[s], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // P^T = exp2(S^T * scale * log2 e - LSE * log2 e), dS^T = P^T (dP^T - delta)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sp[r] = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
+        if (!full) {
+          // register r holds key c0 + 8 (r / 4) + 4 h2 + r % 4
+          const int rl = lo - c0 - 4 * h2, rh = hi - c0 - 4 * h2;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            sp[r] = (off >= rl && off < rh) ? sp[r] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = sp[r] * (dp[r] + ndlt);
         const bf16x8 sb0 = pack_bf16x8(dp, 0), sb1 = pack_bf16x8(dp, 8);
-        mfma_burst_begin();
+        // dQ^T += K^T dS^T
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+          const uint16_t* kr = Ks + (32 * kb + 16 * ks) * D;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            dq[db] = mfma32(lds_trA<D>(Ks, 32 * kb + 16 * ks, 32 * db, lane), ks ? sb1 : sb0, dq[db]);
+            dq[db] = mfma32(lds_trA_at(kr + toff[db][0], kr + toff[db][1]), ks ? sb1 : sb0, dq[db]);
         }
-        mfma_burst_end();
       }
     }
 
     wait_vmem();
     __syncthreads();
+  };
+
+  for (int i = 0; i < ntiles; i += 2) {
+    tile(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < ntiles) tile(std::integral_constant<int, 1>{}, i + 1);
   }
 
   if (wave_active && p < a.n) {
