@@ -110,6 +110,62 @@ def cpu_baseline(w, q, k, v, do, target_s=10.0, chunk=2048):
     }
 
 
+class ClockSampler:
+    """Polls the GPU's graphics clock (amdsmi, SYS clock, MHz) from a
+    background thread while kernels run: the rates above are only comparable
+    at known clocks.  Reports None where amdsmi is unavailable."""
+
+    def __init__(self, period_s: float = 0.005):
+        import threading
+        self.samples = []
+        self.period = period_s
+        self.handle = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                self.amdsmi = amdsmi
+                self.handle = handles[0]
+                self.read()
+        except Exception:
+            self.handle = None
+
+    def read(self):
+        info = self.amdsmi.amdsmi_get_clock_info(self.handle, self.amdsmi.AmdSmiClkType.SYS)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.handle is None:
+            return
+        self._stop.clear()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=1.0)
+            self._thread = None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples), "samples": len(self.samples), "source": "amdsmi SYS clock"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -178,12 +234,15 @@ def main():
         diffusion_step()
     torch.cuda.synchronize()
     evs = [new_events() for _ in range(args.steps)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         diffusion_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.stop()
     ms_per_step = wall * 1e3 / args.steps
 
     def split(ev_list):
@@ -233,6 +292,7 @@ def main():
         torch.cuda.synchronize()
         reps = max(1, int(math.ceil(args.round_ms / max(ms_per_step, 1e-3))))
         rounds = {"diff": [], "causal": []}
+        clock.start()
         for _ in range(args.rounds):
             for name, fn in (("diff", diffusion_step), ("causal", causal_step)):
                 ev_list = [new_events() for _ in range(reps)]
@@ -243,6 +303,7 @@ def main():
                 f = sum(per["fwd"]) / reps
                 bwd = sum(per["bwd_preprocess"][i] + per["bwd_dkdv"][i] + per["bwd_dq"][i] for i in range(reps)) / reps
                 rounds[name].append((f, bwd))
+        clock.stop()
         med = {name: (statistics.median(x[0] for x in r), statistics.median(x[1] for x in r),
                       statistics.median(x[0] + x[1] for x in r)) for name, r in rounds.items()}
         Pc = n * (n + 1) // 2
@@ -292,6 +353,7 @@ def main():
         "interleaved_medians": medians,
         "kernel_avg_ms": kern_avg,
         "device": torch.cuda.get_device_name(dev),
+        "sclk": clock.summary(),
     }
     print(json.dumps(line))
 
