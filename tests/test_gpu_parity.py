@@ -26,7 +26,7 @@ import torch
 
 import oracle
 import block_diffusion_lm_amd as bd
-from workloads import WORKLOADS, make_inputs, make_workload_inputs
+from workloads import WORKLOADS, make_causal_view, make_inputs, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,22 @@ def test_scale_other_than_default():
     q, k, v, do = make_inputs(1, 70, 2, 64, seed=9001)
     res = run_diffusion(q, k, v, do, 5, 0.3)
     compare_full(res, q, k, v, do, 5, 0.3, "scale 0.3")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_negative_scale(D):
+    # the forward folds the sign into Q; the backward uses the signed factor
+    q, k, v, do = make_inputs(1, 150, 2, D, seed=9002)
+    res = run_diffusion(q, k, v, do, 16, -0.2)
+    compare_full(res, q, k, v, do, 16, -0.2, f"scale -0.2 D{D}")
+    cq, ck, cv, cdo = (make_causal_view(x) for x in (q, k, v, do))
+    res = run_causal(cq, ck, cv, cdo, -0.2)
+    f = oracle.to_f64
+    O, L = oracle.batched(oracle.causal_forward, f(cq), f(ck), f(cv), scale=-0.2)
+    dQ, dK, dV = oracle.batched(oracle.causal_backward, f(cq), f(ck), f(cv), f(cdo), scale=-0.2)
+    check_fwd(res["out"], res["lse"], O, L, f"causal scale -0.2 D{D}")
+    for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
+        check_grad(res[name], ref, name, f"causal scale -0.2 D{D}")
 
 
 # ---------------------------------------------------------------------------
