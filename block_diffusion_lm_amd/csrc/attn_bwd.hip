@@ -131,7 +131,10 @@ struct DkdvCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int NBUF = 3;          // Q / dO ring depth
-  using Tile = DirectTile<BQ, D, NT>;
+  // The P-waves (threads [0, NT / 2)) load the tiles: they finish their
+  // share of a step earlier, so they also absorb the wait for the next
+  // tile, and the barrier that ends the step publishes it to the dS-waves.
+  using Tile = DirectTile<BQ, D, NT / 2>;
   static constexpr int BUF = 2 * Tile::ELEMS;   // Q then dO
   static constexpr int FBUF = 2 * BQ;           // lse2 then -delta
   static constexpr int PXS = NPAIR * QB * 2 * 64;  // 16-byte slots of one P exchange buffer
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) acc[i] = zero16();
 
-  if (ntiles > 0) issue_tile(0, 0);
+  if (pwave && ntiles > 0) issue_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     floatx16 dpr[C::QB];
     bool pact[C::QB] = {false, false};
     for (int j = 0; j <= ntiles; ++j) {
-      if (j + 1 < ntiles) issue_tile(j + 1, slot_next);
+      if (PW && j + 1 < ntiles) issue_tile(j + 1, slot_next);
       const int slot_prev = slot == 0 ? C::NBUF - 1 : slot - 1;
       if constexpr (PW) {
         if (j < ntiles) {
