@@ -251,12 +251,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
     __syncthreads();
   };
 
-  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three tiles");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of two to four tiles");
   for (int i = 0; i < ntiles; i += NBUF) {
-    tile(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < ntiles) tile(std::integral_constant<int, 1>{}, i + 1);
-    if constexpr (NBUF == 3)
-      if (i + 2 < ntiles) tile(std::integral_constant<int, 2 % NBUF>{}, i + 2);
+    static_for<NBUF>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if (i + J < ntiles) tile(std::integral_constant<int, J>{}, i + J);
+    });
   }
 
   // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2.
@@ -290,13 +290,16 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
 #ifndef BDATTN_FWD_NW
 #define BDATTN_FWD_NW 4
 #endif
+#ifndef BDATTN_FWD_BN
+#define BDATTN_FWD_BN 64
+#endif
 #ifndef BDATTN_FWD_NBUF
 #define BDATTN_FWD_NBUF 2
 #endif
 
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
-  if (D == 64) return launch_fwd_t<64, 64, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
-  return launch_fwd_t<128, 64, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  if (D == 64) return launch_fwd_t<64, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }
 
 }  // namespace bd

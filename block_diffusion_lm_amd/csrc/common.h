@@ -14,6 +14,8 @@
 // permutation of the D layout, so scores never leave registers.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -142,6 +144,17 @@ __device__ __forceinline__ void lds_direct4(rsrc_t r, uint32_t lds_wave, uint32_
 template <typename T>
 __device__ __forceinline__ void settle(T& v) {
   asm volatile("" : "+v"(v));
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled at compile
+// time (for code whose indices must be constants, such as LDS buffer
+// numbers that become immediate address offsets).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 // Wait until this wave's loads into LDS (and all its other vector memory
