@@ -17,16 +17,17 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest element count of one [B][T][H][D] tensor the kernels index
-// (64-bit offsets are used, but the grid and the per-row statistics use
-// 32-bit block counts).
+// Limits of one [B][T][H][D] tensor.  Offsets are 64-bit, but grid sizes
+// are 32-bit: the attention grids have at most ceil(T / 64) * B * H blocks
+// and the preprocess grid one block per 16 or 32 rows, so B * T * H rows
+// are capped at 2^31 - 1 (512 GB of bf16 at D = 128, more than a GPU holds).
 int check_shape(int B, int T, int H, int D) {
   if (B < 1 || T < 1 || H < 1) return BDATTN_ERR_INVALID;
   if (D != 64 && D != 128) return BDATTN_ERR_UNSUPPORTED;
   const long long tiles = ((long long)T + 63) / 64 * B * H;
   if (tiles > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
   const long long rows = (long long)B * T * H;
-  if (rows > (1LL << 40)) return BDATTN_ERR_INVALID;
+  if (rows > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
   // The kernels address one half of one sample (all heads) through a 32-bit
   // buffer range: T/2 (or T) tokens x H x D bf16 must stay below 2 GiB.
   if ((long long)T * H * D * 2 >= (1LL << 31)) return BDATTN_ERR_UNSUPPORTED;

@@ -57,6 +57,8 @@ def _fwd(**kw):
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
     (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
     (dict(n=2 ** 22, H=2, D=128), UNSUPPORTED),
+    # 2^31 rows in all (32-bit grid of the preprocess kernel), each sample small
+    (dict(B=2 ** 20, n=1024, H=1, D=64), INVALID),
 ])
 def test_fwd_rejects(kw, want):
     assert _fwd(**kw) == want
