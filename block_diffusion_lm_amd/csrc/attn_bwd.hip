@@ -327,17 +327,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
       }
     };
 
-    // ring slots (tile index mod NBUF) of the tile issued in this step and
-    // of tile j
-    int slot_next = 1;
-    int slot = 0;
-    auto advance = [](int x) { return x == C::NBUF - 1 ? 0 : x + 1; };
     // dS-wave: dP of the previous tile and which of its blocks are active
     floatx16 dpr[C::QB];
     bool pact[C::QB] = {false, false};
-    for (int j = 0; j <= ntiles; ++j) {
+    // Step j; tile j sits in ring slot SLOT = j mod NBUF, a compile-time
+    // constant (the loop below is unrolled by the ring depth) so that every
+    // LDS read is a lane register plus an immediate offset.
+    auto step_j = [&](auto slotc, int j) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slotc)::value;
+      constexpr int slot_next = (slot + 1) % C::NBUF;
+      constexpr int slot_prev = (slot + C::NBUF - 1) % C::NBUF;
       if (PW && j + 1 < ntiles) issue_tile(j + 1, slot_next);
-      const int slot_prev = slot == 0 ? C::NBUF - 1 : slot - 1;
       if constexpr (PW) {
         if (j < ntiles) {
           const uint16_t* Tb = smem + slot * C::BUF;
@@ -430,8 +430,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
       }
       wait_vmem();
       __syncthreads();
-      slot_next = advance(slot_next);
-      slot = advance(slot);
+    };
+    static_assert(C::NBUF == 3, "the step loop is unrolled by the ring depth");
+    for (int j0 = 0; j0 <= ntiles; j0 += C::NBUF) {
+      step_j(std::integral_constant<int, 0>{}, j0);
+      if (j0 + 1 <= ntiles) step_j(std::integral_constant<int, 1>{}, j0 + 1);
+      if (j0 + 2 <= ntiles) step_j(std::integral_constant<int, 2>{}, j0 + 2);
     }
   };
   if (pwave)
