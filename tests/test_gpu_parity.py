@@ -233,6 +233,35 @@ def test_autograd_wrapper_matches_entry_points():
         assert torch.equal(t.grad.cpu(), ref[name]), name
 
 
+def test_backward_stages_on_two_streams():
+    # after stage 0 the dK/dV and dQ stages read only inputs and the
+    # workspace and write disjoint outputs: run them concurrently on two
+    # (default-priority) streams and compare with the one-stream backward
+    dev = _dev()
+    w = WORKLOADS["c2"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    ref = run_diffusion(q, k, v, do, w.b, scale)
+    B, T, H, D = q.shape
+    n = T // 2
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    out, lse = ref["out"].to(dev), ref["lse"].to(dev)
+    dq, dk, dv = (torch.zeros_like(q) for _ in range(3))
+    ws = torch.empty(bd.diffusion_attn_bwd_workspace_size(B, n, H, D), dtype=torch.uint8, device=dev)
+    MD = bd.MODE_DIFFUSION
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s1)
+    with torch.cuda.stream(s2):
+        bd.bdattn_bwd_stage(MD, 2, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s2)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(t.cpu(), ref[name]), name
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads
 # ---------------------------------------------------------------------------
