@@ -209,7 +209,7 @@ def main():
         bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
         if ev is not None:
             ev[1].record()
-        for stage in range(3):
+        for stage in range(2):
             bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, b, scale, ws, ws_bytes)
             if ev is not None:
                 ev[2 + stage].record()
@@ -220,14 +220,14 @@ def main():
         bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
         if ev is not None:
             ev[1].record()
-        for stage in range(3):
+        for stage in range(2):
             bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, 2 * B, n, H, D, 1,
                                 scale, cws)
             if ev is not None:
                 ev[2 + stage].record()
 
     def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
     # ---- warm-up, then exactly K timed steps --------------------------------
     for _ in range(args.warmup):
@@ -246,12 +246,11 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     def split(ev_list):
-        per = {"fwd": [], "bwd_preprocess": [], "bwd_dkdv": [], "bwd_dq": []}
+        per = {"fwd": [], "bwd_dq": [], "bwd_dkdv": []}
         for ev in ev_list:
             per["fwd"].append(ev[0].elapsed_time(ev[1]))
-            per["bwd_preprocess"].append(ev[1].elapsed_time(ev[2]))
+            per["bwd_dq"].append(ev[1].elapsed_time(ev[2]))
             per["bwd_dkdv"].append(ev[2].elapsed_time(ev[3]))
-            per["bwd_dq"].append(ev[3].elapsed_time(ev[4]))
         return per
 
     kern = split(evs)
@@ -263,7 +262,7 @@ def main():
     F_bwd = 2.5 * F_fwd
     value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
     t_fwd = kern_avg["fwd"]
-    t_bwd = kern_avg["bwd_preprocess"] + kern_avg["bwd_dkdv"] + kern_avg["bwd_dq"]
+    t_bwd = kern_avg["bwd_dq"] + kern_avg["bwd_dkdv"]
 
     # ---- the dominant kernel against its roofline ---------------------------
     per_kernel_flops = {"fwd": 2 * 2.0 * P * D * H * B,        # S = QK^T, O = PV
@@ -301,7 +300,7 @@ def main():
                 torch.cuda.synchronize()
                 per = split(ev_list)
                 f = sum(per["fwd"]) / reps
-                bwd = sum(per["bwd_preprocess"][i] + per["bwd_dkdv"][i] + per["bwd_dq"][i] for i in range(reps)) / reps
+                bwd = sum(per["bwd_dq"][i] + per["bwd_dkdv"][i] for i in range(reps)) / reps
                 rounds[name].append((f, bwd))
         clock.stop()
         med = {name: (statistics.median(x[0] for x in r), statistics.median(x[1] for x in r),

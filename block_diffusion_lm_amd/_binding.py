@@ -166,7 +166,7 @@ def causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, scale, work
 
 def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size,
                      scale, workspace, workspace_bytes=None, stream=None):
-    """One backward kernel (0: -delta and lse2, 1: dK/dV, 2: dQ); n is S in causal mode."""
+    """One backward kernel (0: dQ, also writing -delta and lse2; 1: dK/dV); n is S in causal mode."""
     T = 2 * n if mode == MODE_DIFFUSION else n
     shp = (B, T, H, D)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),

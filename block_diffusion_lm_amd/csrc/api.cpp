@@ -18,9 +18,9 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Limits of one [B][T][H][D] tensor.  Offsets are 64-bit, but grid sizes
-// are 32-bit: the attention grids have at most ceil(T / 64) * B * H blocks
-// and the preprocess grid one block per 16 or 32 rows, so B * T * H rows
-// are capped at 2^31 - 1 (512 GB of bf16 at D = 128, more than a GPU holds).
+// are 32-bit: the attention grids have at most ceil(T / 64) * B * H blocks.
+// B * T * H rows are capped at 2^31 - 1 (512 GB of bf16 at D = 128, more
+// than a GPU holds) so that any per-row count fits a 32-bit int.
 int check_shape(int B, int T, int H, int D) {
   if (B < 1 || T < 1 || H < 1) return BDATTN_ERR_INVALID;
   if (D != 64 && D != 128) return BDATTN_ERR_UNSUPPORTED;
@@ -168,7 +168,7 @@ int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const vo
                      void* dv, int B, int n, int H, int D, int block_size, float scale,
                      void* workspace, size_t workspace_bytes_, void* stream) {
   if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
-  if (stage < 0 || stage > 2) return BDATTN_ERR_INVALID;
+  if (stage < 0 || stage > 1) return BDATTN_ERR_INVALID;
   return bwd_common(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D,
                     mode == bd::MODE_CAUSAL ? 1 : block_size, scale, workspace, workspace_bytes_,
                     stream);

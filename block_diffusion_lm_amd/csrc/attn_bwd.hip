@@ -1,12 +1,13 @@
-// attn_bwd.hip -- backward pass, split in three kernels:
+// attn_bwd.hip -- backward pass, split in two kernels:
 //
-//   preprocess : per query row, -delta_i = -(dO_i . O_i) and lse_i * log2(e)
-//                (both float32, into the caller's workspace);
-//   dkdv       : one workgroup per 128-key tile; it walks the query tiles
-//                that see its keys and accumulates dV = P^T dO and
-//                dK = scale * dS^T Q in registers;
-//   dq         : one workgroup per 128-row query tile; it walks the key
-//                tiles its rows see and accumulates dQ = scale * dS K.
+//   dq   : one workgroup per 128-row query tile.  Each wave first computes,
+//          for its 32 rows, delta_i = dO_i . O_i and lse_i * log2(e) and
+//          stores -delta and lse2 (float32) in the caller's workspace; then
+//          it walks the key tiles its rows see and accumulates
+//          dQ = scale * dS K;
+//   dkdv : one workgroup per 128-key tile (runs after dq, reading the
+//          workspace); it walks the query tiles that see its keys and
+//          accumulates dV = P^T dO and dK = scale * dS^T Q in registers.
 //
 // FlashAttention: Exact Attention Without Materialization, section 4.5:
 // the probabilities are recomputed on chip from Q, K and the saved
@@ -40,39 +41,6 @@ namespace bd {
 
 __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
   return (a.mode == MODE_DIFFUSION && half == CLEAN) ? a.n : 0;
-}
-
-// ---------------------------------------------------------------------------
-// -delta_i = -sum_d dO[i][d] * O[i][d] and lse2_i = lse_i * log2(e); one
-// 16-byte chunk per lane, rows of D / 8 lanes reduced with shuffles.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a, long long rows) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 ov = ld16(a.o + row * D + c * 8);
-    const u32x4 gv = ld16(a.dout + row * D + c * 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += __builtin_bit_cast(float, ov[w] << 16) * __builtin_bit_cast(float, gv[w] << 16);
-      acc += __builtin_bit_cast(float, ov[w] & 0xffff0000u) * __builtin_bit_cast(float, gv[w] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && c == 0) {
-    // row = (b * T + t) * H + h  ->  statistic index (b * H + h) * T + t
-    const long long h = row % a.H;
-    const long long bt = row / a.H;
-    const long long t = bt % a.T;
-    const long long b = bt / a.T;
-    const long long si = (b * a.H + h) * a.T + t;
-    a.ndelta[si] = -acc;
-    a.lse2[si] = a.lse_in[si] * kLog2e;
-  }
 }
 
 // Per-segment scalars.  A key-stationary wave needs, for each query half it
@@ -513,23 +481,48 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   const bool wave_active = pw0 < a.n;
   const int p = pw0 + l32;
 
-  // Q and dO as B operands; rows past the half read as zero, and so do their
+  // Q and dO as B operands: lane (row p, half h2) holds 16-byte chunks
+  // 2s + h2 of its row.  Rows past the half read as zero, and so do their
   // statistics, which makes their dS zero.
+  //
+  // The row statistics: delta_p = dO_p . O_p from the same chunks of O
+  // (FlashAttention section 4.5: rowsum(P o dP) equals dO . O), summed over
+  // the lane pair (p, 0) and (p, 1); lse2_p = lse_p * log2(e).  Both go to
+  // the workspace for the dK/dV kernel (-delta, so that it can start its dP
+  // accumulators there).
   bf16x8 qf[C::KS], gf[C::KS];
   float lse2, ndlt;
   {
     const size_t qb = (sample0 + qoff) * rs + (size_t)hh * D;
     const rsrc_t rq = make_rsrc(a.q + qb, half_bytes);
     const rsrc_t rg = make_rsrc(a.dout + qb, half_bytes);
+    const rsrc_t ro = make_rsrc(a.o + qb, half_bytes);
+    u32x4 ov[C::KS];
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const uint32_t off = (uint32_t)p * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u;
       qf[s] = as_bf16x8(buf_ld16(rq, off, 0));
       gf[s] = as_bf16x8(buf_ld16(rg, off, 0));
+      ov[s] = buf_ld16(ro, off, 0);
     }
     const size_t sb = ((size_t)bi * a.H + hh) * a.T + qoff;
-    lse2 = buf_ldf(make_rsrc(a.lse2 + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
-    ndlt = buf_ldf(make_rsrc(a.ndelta + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+    const float lse = buf_ldf(make_rsrc(a.lse_in + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+    float dpart = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const u32x4 g = __builtin_bit_cast(u32x4, gf[s]);
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        dpart += __builtin_bit_cast(float, ov[s][w2] << 16) * __builtin_bit_cast(float, g[w2] << 16);
+        dpart += __builtin_bit_cast(float, ov[s][w2] & 0xffff0000u) * __builtin_bit_cast(float, g[w2] & 0xffff0000u);
+      }
+    }
+    ndlt = -halves_sum(dpart);
+    lse2 = lse * kLog2e;
+    if (wave_active && p < a.n && h2 == 0) {
+      a.ndelta[sb + p] = ndlt;
+      a.lse2[sb + p] = lse2;
+    }
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       settle(qf[s]);
@@ -663,20 +656,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
 template <int D>
 static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
   if (stage == 0) {
-    const long long rows = (long long)a.B * a.T * a.H;
-    constexpr int rows_per_block = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                       dim3(256), 0, s, a, rows);
-  } else if (stage == 1) {
-    using KC = DkdvCfg<D>;
-    const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
-    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
-  } else {
     using QC = DqCfg<D>;
     const int qtiles = (a.n + QC::BM - 1) / QC::BM;
     const long long qblocks = (long long)qtiles * a.nhalves * a.B * a.H;
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)qblocks), dim3(QC::NT), 0, s, a, qtiles);
+  } else {
+    using KC = DkdvCfg<D>;
+    const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
+    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
   }
   return hipGetLastError();
 }
@@ -686,7 +674,7 @@ hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s) 
 }
 
 hipError_t launch_bwd(const AttnArgs& a, int D, hipStream_t s) {
-  for (int stage = 0; stage < 3; ++stage) {
+  for (int stage = 0; stage < 2; ++stage) {
     hipError_t e = launch_bwd_stage(a, D, stage, s);
     if (e != hipSuccess) return e;
   }

@@ -38,7 +38,7 @@ struct AttnArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, int D, hipStream_t s);
-// One backward kernel: 0 = preprocess (-delta, lse2), 1 = dK/dV, 2 = dQ.
+// One backward kernel: 0 = dQ (also writes -delta and lse2), 1 = dK/dV.
 hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s);
 
 }  // namespace bd

@@ -31,9 +31,8 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # bench.py's names of the kernels it times, and the symbols they map to
 KERNELS = {
     "fwd": "fwd_kernel",
-    "bwd_preprocess": "bwd_preprocess_kernel",
-    "bwd_dkdv": "bwd_dkdv",
     "bwd_dq": "bwd_dq_kernel",
+    "bwd_dkdv": "bwd_dkdv",
 }
 COPY_SYMBOL = "copyBuffer"
 

@@ -101,13 +101,12 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
  * One stage of the backward pass (same arguments as diffusion_attn_bwd /
  * causal_attn_bwd; mode 0 = diffusion with block_size, 1 = causal with n = S
  * and block_size ignored):
- *   stage 0 -- writes the per-row -delta_i = -(dout_i . out_i) and lse_i * log2(e)
- *              to the workspace;
- *   stage 1 -- dK and dV (reads the workspace);
- *   stage 2 -- dQ (reads the workspace).
- * The full backward is stages 0, 1, 2 on one stream.  Stages 1 and 2 read
- * only inputs and the workspace and write disjoint outputs, so after stage 0
- * they may run concurrently on two streams.
+ *   stage 0 -- dQ; it also writes the per-row -delta_i = -(dout_i . out_i)
+ *              and lse_i * log2(e) to the workspace;
+ *   stage 1 -- dK and dV (reads the workspace written by stage 0).
+ * The full backward is stages 0 and 1, in that order, on one stream (or
+ * with stage 1 ordered after stage 0).  Other stage numbers return
+ * BDATTN_ERR_INVALID.
  */
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,

@@ -57,7 +57,7 @@ def _fwd(**kw):
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
     (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
     (dict(n=2 ** 22, H=2, D=128), UNSUPPORTED),
-    # 2^31 rows in all (32-bit grid of the preprocess kernel), each sample small
+    # 2^31 rows in all (over the 32-bit row limit), each sample small
     (dict(B=2 ** 20, n=1024, H=1, D=64), INVALID),
 ])
 def test_fwd_rejects(kw, want):
@@ -78,6 +78,13 @@ def _bwd(**kw):
 ])
 def test_bwd_rejects(kw, want):
     assert _bwd(**kw) == want
+
+
+@pytest.mark.parametrize("stage", [-1, 2, 3])
+def test_bwd_stage_rejects_unknown_stage(stage):
+    # stage 0 is dQ (with the row statistics), stage 1 dK/dV; nothing else
+    lib = bd.lib()
+    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), 1, 16, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
 
 
 def test_causal_rejects():

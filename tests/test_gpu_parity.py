@@ -233,10 +233,10 @@ def test_autograd_wrapper_matches_entry_points():
         assert torch.equal(t.grad.cpu(), ref[name]), name
 
 
-def test_backward_stages_on_two_streams():
-    # after stage 0 the dK/dV and dQ stages read only inputs and the
-    # workspace and write disjoint outputs: run them concurrently on two
-    # (default-priority) streams and compare with the one-stream backward
+def test_backward_stages_in_order_on_two_streams():
+    # stage 0 (dQ, which also writes the row statistics) on one stream, stage
+    # 1 (dK/dV, which reads them) on another, ordered by an event: the same
+    # bits as the one-call backward
     dev = _dev()
     w = WORKLOADS["c2"]
     q, k, v, do = make_workload_inputs(w)
@@ -250,13 +250,14 @@ def test_backward_stages_on_two_streams():
     ws = torch.empty(bd.diffusion_attn_bwd_workspace_size(B, n, H, D), dtype=torch.uint8, device=dev)
     MD = bd.MODE_DIFFUSION
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    torch.cuda.synchronize()
-    bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws)
+    done0 = torch.cuda.Event()
     torch.cuda.synchronize()
     with torch.cuda.stream(s1):
-        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s1)
+        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s1)
+        done0.record(s1)
+    s2.wait_event(done0)
     with torch.cuda.stream(s2):
-        bd.bdattn_bwd_stage(MD, 2, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s2)
+        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s2)
     torch.cuda.synchronize()
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(t.cpu(), ref[name]), name
