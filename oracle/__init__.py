@@ -23,6 +23,10 @@ from .attention import (  # noqa: F401
     diffusion_grad_kv_cols,
     causal_forward,
     causal_backward,
+    kv_head_of,
+    grouped_forward,
+    grouped_backward,
+    grouped_grad_kv_cols,
     batched,
     to_f64,
 )

@@ -198,6 +198,81 @@ def causal_backward(q, k, v, dout, scale: float):
 
 
 # --------------------------------------------------------------------------
+# Grouped-query attention: H query heads share H_kv key/value heads
+# --------------------------------------------------------------------------
+#
+# Fast Diffusion Attention, "Ampere and Ada" (the GQA-grouped backward):
+# several query heads read one key/value head, and that head's dK / dV is
+# the sum of what each of those query heads contributes (the chain rule for
+# a shared input).  Which query heads form a group is not stated on the
+# pages; the reading taken is flash-attention's (whose call shape the pages
+# follow): H_kv consecutive runs of H / H_kv query heads, run j reading
+# key/value head j.
+
+def kv_head_of(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h."""
+    if H_kv < 1 or H % H_kv or not 0 <= h < H:
+        raise ValueError("need 1 <= H_kv, H divisible by H_kv and 0 <= h < H")
+    return h // (H // H_kv)
+
+
+def grouped_forward(fn: Callable, q, k, v, heads: Optional[Sequence[Tuple[int, int]]] = None, **kw):
+    """(O, LSE) of q (B, T, H, D) against k, v (B, T, H_kv, D).
+
+    ``fn`` is a one-head forward such as ``diffusion_forward``; query head h
+    of sample bi runs it with key/value head ``kv_head_of(h)``.  ``heads``
+    restricts the work to the listed (sample, query head) pairs (the other
+    entries are NaN).
+    """
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    O = np.full((B, T, H, D), np.nan)
+    L = np.full((B, H, T), np.nan)
+    todo = heads if heads is not None else [(bi, h) for bi in range(B) for h in range(H)]
+    for bi, h in todo:
+        j = kv_head_of(h, H, H_kv)
+        O[bi, :, h], L[bi, h] = fn(q[bi, :, h], k[bi, :, j], v[bi, :, j], **kw)
+    return O, L
+
+
+def grouped_backward(fn: Callable, q, k, v, dout, **kw):
+    """(dq, dk, dv) for q, dout (B, T, H, D) and k, v (B, T, H_kv, D).
+
+    ``fn`` is a one-head backward such as ``diffusion_backward``.  dq of a
+    query head is that head's own; dk and dv of key/value head j sum the
+    contributions of every query head of its group.
+    """
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for bi in range(B):
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            gq, gk, gv = fn(q[bi, :, h], k[bi, :, j], v[bi, :, j], dout[bi, :, h], **kw)
+            dq[bi, :, h] = gq
+            dk[bi, :, j] += gk
+            dv[bi, :, j] += gv
+    return dq, dk, dv
+
+
+def grouped_grad_kv_cols(qs, k, v, douts, outs, lses, b: int, scale: float, cols: Sequence[int]):
+    """dK and dV of the key columns ``cols`` of one key/value head.
+
+    ``qs``, ``douts``, ``outs``, ``lses``: one entry per query head of the
+    group (each as ``diffusion_grad_kv_cols`` takes them); the result is the
+    sum of the heads' contributions.
+    """
+    dk = dv = 0.0
+    for qh, dh, oh, lh in zip(qs, douts, outs, lses):
+        gk, gv = diffusion_grad_kv_cols(qh, k, v, dh, oh, lh, b, scale, cols)
+        dk = dk + gk
+        dv = dv + gv
+    return dk, dv
+
+
+# --------------------------------------------------------------------------
 # (batch, seq, heads, dim) helpers
 # --------------------------------------------------------------------------
 

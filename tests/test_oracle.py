@@ -61,6 +61,27 @@ def test_visible_pairs_closed_form_all_workloads():
             assert total == w.n * w.n + w.n * w.b
 
 
+def _prose_mask(n, b):
+    """The mask written from the prose of 'Block diffusion in one picture',
+    one explicit list of blocks at a time."""
+    blocks = _blocks(n, b)
+    want = np.zeros((2 * n, 2 * n), dtype=bool)
+    for i, blk in enumerate(blocks):
+        for r in blk:
+            # noisy row: its own noisy block, both directions
+            for c in blk:
+                want[r, c] = True
+            # noisy row: every clean block strictly before block i
+            for earlier in blocks[:i]:
+                for c in earlier:
+                    want[r, n + c] = True
+            # clean row: its own clean block and the earlier clean blocks
+            for earlier in blocks[: i + 1]:
+                for c in earlier:
+                    want[n + r, n + c] = True
+    return want
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 11])
 def test_mask_matches_block_description_bruteforce(n):
     """Tiny sizes: the mask equals the prose of 'Block diffusion in one picture'
@@ -68,20 +89,7 @@ def test_mask_matches_block_description_bruteforce(n):
     for b in range(1, n + 3):
         M = oracle.block_diffusion_mask(n, b)
         blocks = _blocks(n, b)
-        want = np.zeros((2 * n, 2 * n), dtype=bool)
-        for i, blk in enumerate(blocks):
-            for r in blk:
-                # noisy row: its own noisy block, both directions
-                for c in blk:
-                    want[r, c] = True
-                # noisy row: every clean block strictly before block i
-                for earlier in blocks[:i]:
-                    for c in earlier:
-                        want[r, n + c] = True
-                # clean row: its own clean block and the earlier clean blocks
-                for earlier in blocks[: i + 1]:
-                    for c in earlier:
-                        want[n + r, n + c] = True
+        want = _prose_mask(n, b)
         assert np.array_equal(M, want), (n, b)
         # staircase equivalence ('The right yardstick'): noisy row block i sees
         # i blocks in total, like a causal row over blocks
@@ -327,3 +335,108 @@ def test_inputs_are_seeded_bf16():
         assert torch.equal(x, y)
     c = make_inputs(1, 8, 2, 4, seed=4)
     assert not torch.equal(a[0], c[0])
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention (query heads sharing key/value heads)
+# --------------------------------------------------------------------------
+
+GQA_SHAPES = [(2, 7, 6, 2, 3), (1, 9, 4, 1, 4), (2, 5, 4, 4, 2)]  # B, n, H, H_kv, b
+
+
+@pytest.mark.parametrize("B,n,H,H_kv,b", GQA_SHAPES)
+def test_grouped_oracle_matches_sdpa_gqa(B, n, H, H_kv, b):
+    """torch's scaled_dot_product_attention with enable_gqa (float64, CPU)
+    under the prose mask: the grouped forward, and through autograd the
+    grouped backward, whose dK / dV sum over each group's query heads."""
+    D, scale = 5, 0.55
+    q, k, v, do = make_inputs(B, n, H, D, seed=40 + H_kv, H_kv=H_kv)
+    f = oracle.to_f64
+    O, _ = oracle.grouped_forward(oracle.diffusion_forward, f(q), f(k), f(v), b=b, scale=scale)
+    dq, dk, dv = oracle.grouped_backward(oracle.diffusion_backward, f(q), f(k), f(v), f(do),
+                                         b=b, scale=scale)
+    t = lambda x: x.to(torch.float64).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    tq, tk, tv = t(q), t(k), t(v)
+    mask = torch.from_numpy(_prose_mask(n, b))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale, enable_gqa=True)
+    (o * do.to(torch.float64).permute(0, 2, 1, 3)).sum().backward()
+    back = lambda x: x.permute(0, 2, 1, 3).detach().numpy()
+    np.testing.assert_allclose(O, back(o), atol=1e-12)
+    np.testing.assert_allclose(dq, back(tq.grad), atol=1e-11)
+    np.testing.assert_allclose(dk, back(tk.grad), atol=1e-11)
+    np.testing.assert_allclose(dv, back(tv.grad), atol=1e-11)
+
+
+def test_grouped_head_map_closed_forms():
+    """q = 0 makes each row the mean of its visible values of the key/value
+    head its group reads; shifting the keys of head j by c_j shifts the LSE
+    of query head h by scale * q_h . c_{h // (H / H_kv)}.  Distinct values
+    and shifts per key/value head fix the map for O and for LSE."""
+    B, n, H, H_kv, b, D, scale = 1, 6, 6, 3, 2, 4, 0.9
+    G = H // H_kv
+    v = _rand((B, 2 * n, H_kv, D), 50) + 10.0 * np.arange(H_kv)[None, None, :, None]
+    k = _rand((B, 2 * n, H_kv, D), 51)
+    O, lse = oracle.grouped_forward(oracle.diffusion_forward, np.zeros((B, 2 * n, H, D)), k, v,
+                                    b=b, scale=scale)
+    M = _prose_mask(n, b)
+    for h in range(H):
+        for r in range(2 * n):
+            np.testing.assert_allclose(O[0, r, h], v[0, M[r], h // G].mean(axis=0), atol=1e-12)
+            assert abs(lse[0, h, r] - math.log(M[r].sum())) < 1e-12
+    q = _rand((B, 2 * n, H, D), 52)
+    c = _rand((H_kv, D), 53)
+    _, l1 = oracle.grouped_forward(oracle.diffusion_forward, q, k, v, b=b, scale=scale)
+    _, l2 = oracle.grouped_forward(oracle.diffusion_forward, q, k + c[None, None], v, b=b, scale=scale)
+    for h in range(H):
+        np.testing.assert_allclose(l2[0, h] - l1[0, h], scale * q[0, :, h] @ c[h // G], atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+def test_grouped_gradients_match_central_differences():
+    """Central differences of L = sum(dout * O) over the grouped forward."""
+    B, n, H, H_kv, b, D, scale, eps = 1, 3, 4, 2, 2, 3, 0.7, 1e-6
+    q, do = _rand((B, 2 * n, H, D), 54), _rand((B, 2 * n, H, D), 55)
+    k, v = _rand((B, 2 * n, H_kv, D), 56), _rand((B, 2 * n, H_kv, D), 57)
+    grads = oracle.grouped_backward(oracle.diffusion_backward, q, k, v, do, b=b, scale=scale)
+
+    def loss(qq, kk, vv):
+        O, _ = oracle.grouped_forward(oracle.diffusion_forward, qq, kk, vv, b=b, scale=scale)
+        return float((O * do).sum())
+
+    for which, grad in enumerate(grads):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        err = np.abs(num - grad).max() / np.abs(grad).max()
+        assert err <= 1e-6, (which, err)
+
+
+def test_grouped_sampled_kv_columns_equal_full():
+    B, n, H, H_kv, b, D, scale = 1, 10, 4, 2, 3, 6, 0.4
+    G = H // H_kv
+    q, do = _rand((B, 2 * n, H, D), 58), _rand((B, 2 * n, H, D), 59)
+    k, v = _rand((B, 2 * n, H_kv, D), 60), _rand((B, 2 * n, H_kv, D), 61)
+    O, L = oracle.grouped_forward(oracle.diffusion_forward, q, k, v, b=b, scale=scale)
+    _, dk, dv = oracle.grouped_backward(oracle.diffusion_backward, q, k, v, do, b=b, scale=scale)
+    cols = [0, 2, n - 1, n, 2 * n - 1]
+    for j in range(H_kv):
+        hs = range(j * G, (j + 1) * G)
+        dkc, dvc = oracle.grouped_grad_kv_cols([q[0, :, h] for h in hs], k[0, :, j], v[0, :, j],
+                                               [do[0, :, h] for h in hs], [O[0, :, h] for h in hs],
+                                               [L[0, h] for h in hs], b, scale, cols)
+        np.testing.assert_allclose(dkc, dk[0, cols, j], atol=1e-12)
+        np.testing.assert_allclose(dvc, dv[0, cols, j], atol=1e-12)
+
+
+def test_grouped_inputs_keep_the_mha_draws():
+    """H_kv = H draws the same bits as the plain call; k and v take H_kv heads."""
+    a = make_inputs(1, 8, 4, 4, seed=3)
+    b = make_inputs(1, 8, 4, 4, seed=3, H_kv=4)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    q, k, v, do = make_inputs(1, 8, 4, 4, seed=3, H_kv=2)
+    assert q.shape == do.shape == (1, 16, 4, 4) and k.shape == v.shape == (1, 16, 2, 4)

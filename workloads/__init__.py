@@ -25,7 +25,8 @@ import torch
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
-    """One problem: B samples of 2n tokens, H heads of width D, block size b."""
+    """One problem: B samples of 2n tokens, H query heads of width D reading
+    H_kv key/value heads (0: H_kv = H), block size b."""
 
     name: str
     B: int
@@ -34,13 +35,19 @@ class Workload:
     D: int
     b: int
     seed: int
+    H_kv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
         return (self.B, 2 * self.n, self.H, self.D)
 
     def describe(self) -> str:
-        return (f"{self.name}: B={self.B} n={self.n} (2n={2 * self.n}) H={self.H} "
+        kv = f" H_kv={self.kv_heads}" if self.kv_heads != self.H else ""
+        return (f"{self.name}: B={self.B} n={self.n} (2n={2 * self.n}) H={self.H}{kv} "
                 f"D={self.D} b={self.b} seed={self.seed}")
 
 
@@ -63,11 +70,24 @@ for _D in (64, 128):
         _w = _c5(_D, _b)
         WORKLOADS[_w.name] = _w
 
+# Grouped-query problems (query heads sharing key/value heads): the
+# short-sequence regime in which the pages report the grouped backward's
+# gain (512 to 1K tokens per half), the long-sequence problem with four
+# query heads per key/value head, and multi-query attention (one key/value
+# head).  Parity cases and side measurements; throughput is quoted on c4.
+GQA_WORKLOADS: Dict[str, Workload] = {
+    "g1": Workload("g1", B=8, n=1024, H=32, D=128, b=16, seed=1011, H_kv=8),
+    "g2": Workload("g2", B=2, n=8192, H=32, D=128, b=32, seed=1012, H_kv=8),
+    "g3": Workload("g3", B=4, n=2048, H=16, D=64, b=4, seed=1013, H_kv=1),
+}
+
 LARGEST = "c4"
 
 
-def make_inputs(B: int, n: int, H: int, D: int, seed: int, with_dout: bool = True):
-    """Return bf16 CPU tensors (q, k, v, dout) of shape (B, 2n, H, D).
+def make_inputs(B: int, n: int, H: int, D: int, seed: int, with_dout: bool = True,
+                H_kv: int = 0):
+    """Return bf16 CPU tensors (q, k, v, dout): q and dout of shape
+    (B, 2n, H, D), k and v of shape (B, 2n, H_kv, D) (H_kv = 0: H).
 
     Draw order is fixed (q, k, v, dout) so that every consumer of a seed
     sees the same bits.  ``with_dout=False`` still draws nothing extra and
@@ -75,9 +95,10 @@ def make_inputs(B: int, n: int, H: int, D: int, seed: int, with_dout: bool = Tru
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    shape = (B, 2 * n, H, D)
+    kv = H_kv or H
+    shapes = [(B, 2 * n, H, D), (B, 2 * n, kv, D), (B, 2 * n, kv, D), (B, 2 * n, H, D)]
     out = []
-    for _ in range(4 if with_dout else 3):
+    for shape in shapes[:4 if with_dout else 3]:
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         out.append(x.to(torch.bfloat16))
     if not with_dout:
@@ -86,7 +107,7 @@ def make_inputs(B: int, n: int, H: int, D: int, seed: int, with_dout: bool = Tru
 
 
 def make_workload_inputs(w: Workload, with_dout: bool = True):
-    return make_inputs(w.B, w.n, w.H, w.D, w.seed, with_dout=with_dout)
+    return make_inputs(w.B, w.n, w.H, w.D, w.seed, with_dout=with_dout, H_kv=w.H_kv)
 
 
 def make_causal_view(x: torch.Tensor) -> torch.Tensor:
