@@ -2,8 +2,9 @@
 """Benchmark of block-diffusion attention (forward + backward) on one MI355X.
 
 One step is the whole hot path on one batch: the forward kernel, then the
-three backward kernels (delta, dK/dV, dQ), all through the C ABI of
-libbdattn.so on torch's current stream, with inputs resident in HBM.
+two backward kernels (dQ, which also computes each row's delta and base-2
+log-sum-exp, then dK/dV), all through the C ABI of libbdattn.so on torch's
+current stream, with inputs resident in HBM.
 
 Throughput counts visible (query, key) pairs only (Fast Diffusion
 Attention, "The right yardstick"): 4 * pairs * headdim * heads * batch flops
@@ -14,7 +15,12 @@ in one process and reported as medians (the pages' protocol for clocks that
 follow power draw).
 
 Prints one JSON line.  Default workload: the long-sequence problem
-(B=2, n=8192, H=32, D=128, block size 32).
+(B=2, n=8192, H=32, D=128, block size 32).  The grouped-query workloads
+(g1..g3: query heads sharing key/value heads) also report the backward
+time of the same kernels run ungrouped, on key/value heads repeated to H
+(without the reduction of dK / dV over the group that this would still
+need): the saving of the grouped backward (Fast Diffusion Attention,
+"Ampere and Ada").
 """
 from __future__ import annotations
 
@@ -69,14 +75,15 @@ def cpu_baseline(w, q, k, v, do, target_s=10.0, chunk=2048):
     except Exception:  # pragma: no cover
         cores = 1
     n, scale = w.n, 1.0 / math.sqrt(w.D)
+    G = w.H // w.kv_heads
     pairs, chunks, heads = 0, 0, 0
     t_fwd = t_bwd = 0.0
     t_start = time.perf_counter()
     done = False
     for bi in range(w.B):
         for hi in range(w.H):
-            f = lambda x: oracle.to_f64(x[bi, :, hi])
-            qh, kh, vh, dh = f(q), f(k), f(v), f(do)
+            qh, dh = oracle.to_f64(q[bi, :, hi]), oracle.to_f64(do[bi, :, hi])
+            kh, vh = oracle.to_f64(k[bi, :, hi // G]), oracle.to_f64(v[bi, :, hi // G])
             for r0 in range(0, 2 * n, chunk):
                 rows = np.arange(r0, min(r0 + chunk, 2 * n))
                 M = oracle.block_diffusion_mask(n, w.b, rows)
@@ -177,12 +184,16 @@ def main():
 
     import torch
     import block_diffusion_lm_amd as bd
-    from workloads import WORKLOADS, make_workload_inputs
+    from workloads import GQA_WORKLOADS, WORKLOADS, make_workload_inputs
 
-    w = WORKLOADS[args.workload]
+    all_workloads = {**WORKLOADS, **GQA_WORKLOADS}
+    if args.workload not in all_workloads:
+        print(f"unknown workload {args.workload!r}; known: {', '.join(all_workloads)}", file=sys.stderr)
+        sys.exit(2)
+    w = all_workloads[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B, n, H, D, b = w.B, w.n, w.H, w.D, w.b
+    B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
     T = 2 * n
     scale = 1.0 / math.sqrt(D)
 
@@ -190,39 +201,56 @@ def main():
     q, k, v, do = (x.to(dev) for x in (q_c, k_c, v_c, do_c))
     out = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws_bytes = bd.diffusion_attn_bwd_workspace_size(B, n, H, D)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     # causal yardstick: the same bytes as 2B sequences of n tokens
-    cq, ck, cv, cdo = (x.view(2 * B, n, H, D) for x in (q, k, v, do))
+    cq, cdo = (x.view(2 * B, n, H, D) for x in (q, do))
+    ck, cv = (x.view(2 * B, n, Hkv, D) for x in (k, v))
     cout = torch.empty_like(cq)
     clse = torch.empty((2 * B, H, n), dtype=torch.float32, device=dev)
-    cdq, cdk, cdv = (torch.empty_like(cq) for _ in range(3))
-    cws = torch.empty(bd.causal_attn_bwd_workspace_size(2 * B, n, H, D), dtype=torch.uint8, device=dev)
+    cdq = torch.empty_like(cq)
+    cdk, cdv = torch.empty_like(ck), torch.empty_like(cv)
+    cws = torch.empty(bd.causal_attn_bwd_gqa_workspace_size(2 * B, n, H, Hkv, D), dtype=torch.uint8,
+                      device=dev)
 
     MD, MC = bd.MODE_DIFFUSION, bd.MODE_CAUSAL
+
+    def fwd_diffusion():
+        if Hkv == H:
+            bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+        else:
+            bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
+
+    def fwd_causal():
+        if Hkv == H:
+            bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
+        else:
+            bd.causal_attn_fwd_gqa(cq, ck, cv, cout, clse, 2 * B, n, H, Hkv, D, scale)
 
     def diffusion_step(ev=None):
         if ev is not None:
             ev[0].record()
-        bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+        fwd_diffusion()
         if ev is not None:
             ev[1].record()
         for stage in range(2):
-            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, b, scale, ws, ws_bytes)
+            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, B, n, H, Hkv, D, b, scale,
+                                ws, ws_bytes)
             if ev is not None:
                 ev[2 + stage].record()
 
     def causal_step(ev=None):
         if ev is not None:
             ev[0].record()
-        bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
+        fwd_causal()
         if ev is not None:
             ev[1].record()
         for stage in range(2):
-            bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, 2 * B, n, H, D, 1,
-                                scale, cws)
+            bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, 2 * B, n, H, Hkv,
+                                D, 1, scale, cws)
             if ev is not None:
                 ev[2 + stage].record()
 
@@ -318,6 +346,32 @@ def main():
         ratio = {kname: medians["diffusion_tflops"][kname] / medians["causal_tflops"][kname]
                  for kname in ("fwd", "bwd", "step")}
 
+    # ---- grouped-query workloads: the backward run ungrouped ----------------
+    ungrouped = None
+    if Hkv != H:
+        G = H // Hkv
+        ek, ev_ = (x.repeat_interleave(G, dim=2).contiguous() for x in (k, v))
+        edk, edv = torch.empty_like(q), torch.empty_like(q)
+        times = {"grouped": [], "ungrouped": []}
+        for _ in range(3):
+            for name, kk, vv, gk, gv, hk in (("grouped", k, v, dk, dv, Hkv), ("ungrouped", ek, ev_, edk, edv, H)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 5
+                e0.record()
+                for _ in range(reps):
+                    for stage in range(2):
+                        bd.bdattn_bwd_stage(MD, stage, q, kk, vv, out, do, lse, dq, gk, gv, B, n, H, hk, D, b,
+                                            scale, ws, ws_bytes)
+                e1.record()
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1) / reps)
+        med = {name: statistics.median(x) for name, x in times.items()}
+        ungrouped = {"bwd_ms_grouped": med["grouped"], "bwd_ms_ungrouped": med["ungrouped"],
+                     "speedup": med["ungrouped"] / med["grouped"],
+                     "note": "ungrouped = the same kernels on key/value heads repeated to H, "
+                             "without the dK/dV reduction over the group"}
+        del ek, ev_, edk, edv
+
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -342,7 +396,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.describe(), "global_batch": B, "seq_len": T, "block_size": b,
-                   "heads": H, "headdim": D, "parallelism": "single-gpu"},
+                   "heads": H, "kv_heads": Hkv, "headdim": D, "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fwd_tflops": F_fwd / (t_fwd * 1e-3) / 1e12,
@@ -354,6 +408,8 @@ def main():
         "device": torch.cuda.get_device_name(dev),
         "sclk": clock.summary(),
     }
+    if ungrouped is not None:
+        line["grouped_backward"] = ungrouped
     print(json.dumps(line))
 
 

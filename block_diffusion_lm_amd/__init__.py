@@ -17,11 +17,17 @@ from ._binding import (  # noqa: F401
     bdattn_row_interval,
     bdattn_visible_pairs,
     causal_attn_bwd,
+    causal_attn_bwd_gqa,
+    causal_attn_bwd_gqa_workspace_size,
     causal_attn_bwd_workspace_size,
     causal_attn_fwd,
+    causal_attn_fwd_gqa,
     diffusion_attn_bwd,
+    diffusion_attn_bwd_gqa,
+    diffusion_attn_bwd_gqa_workspace_size,
     diffusion_attn_bwd_workspace_size,
     diffusion_attn_fwd,
+    diffusion_attn_fwd_gqa,
     lib,
     status_string,
 )

@@ -31,7 +31,13 @@ SIGNATURES = {
     "causal_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
-    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 9 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "diffusion_attn_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "diffusion_attn_bwd_gqa": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "causal_attn_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "causal_attn_bwd_gqa": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "diffusion_attn_bwd_gqa_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "causal_attn_bwd_gqa_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "bdattn_fwd_tiles": (_i, [_i, _i, _i, _i, _i, _i, _i, _i32p, _i]),
     "bdattn_bwd_tiles": (_i, [_i, _i, _i, _i, _i, _i, _i, _i32p, _i]),
     "bdattn_row_interval": (_i, [_i, _i, _i, _i, _i, _i, _i32p, _i32p]),
@@ -80,17 +86,21 @@ def _stream_handle(t: torch.Tensor, stream) -> Optional[int]:
     return int(stream)
 
 
-def _want(t: torch.Tensor, name: str, dtype, shape):
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on the GPU, got {t.device}")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _want(*specs):
+    """Check (name, tensor, dtype, shape) specs: dtype, shape and layout of
+    every tensor first, then that all of them live on the GPU."""
+    for name, t, dtype, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU, got {t.device}")
 
 
 def _ptr(t: torch.Tensor) -> int:
@@ -102,10 +112,7 @@ def _ptr(t: torch.Tensor) -> int:
 # ---------------------------------------------------------------------------
 
 def diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, block_size, scale, stream=None):
-    shp = (B, 2 * n, H, D)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-        _want(t, name, torch.bfloat16, shp)
-    _want(lse, "lse", torch.float32, (B, H, 2 * n))
+    _want_fwd(q, k, v, out, lse, B, 2 * n, H, H, D)
     _check(lib().diffusion_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, n, H, D,
                                     block_size, float(scale), _stream_handle(q, stream)),
            "diffusion_attn_fwd")
@@ -117,15 +124,8 @@ def diffusion_attn_bwd_workspace_size(B, n, H, D) -> int:
 
 def diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size, scale,
                        workspace, workspace_bytes=None, stream=None):
-    shp = (B, 2 * n, H, D)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
-                    ("dq", dq), ("dk", dk), ("dv", dv)):
-        _want(t, name, torch.bfloat16, shp)
-    _want(lse, "lse", torch.float32, (B, H, 2 * n))
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    if workspace.device.type != "cuda":
-        raise ValueError("workspace must be on the GPU")
+    workspace_bytes = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, 2 * n, H, H, D, workspace,
+                                workspace_bytes)
     _check(lib().diffusion_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                     _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, D, block_size,
                                     float(scale), _ptr(workspace), int(workspace_bytes),
@@ -134,10 +134,7 @@ def diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_si
 
 
 def causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale, stream=None):
-    shp = (B, S, H, D)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-        _want(t, name, torch.bfloat16, shp)
-    _want(lse, "lse", torch.float32, (B, H, S))
+    _want_fwd(q, k, v, out, lse, B, S, H, H, D)
     _check(lib().causal_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H, D,
                                  float(scale), _stream_handle(q, stream)),
            "causal_attn_fwd")
@@ -149,39 +146,92 @@ def causal_attn_bwd_workspace_size(B, S, H, D) -> int:
 
 def causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, scale, workspace,
                     workspace_bytes=None, stream=None):
-    shp = (B, S, H, D)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
-                    ("dq", dq), ("dk", dk), ("dv", dv)):
-        _want(t, name, torch.bfloat16, shp)
-    _want(lse, "lse", torch.float32, (B, H, S))
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    if workspace.device.type != "cuda":
-        raise ValueError("workspace must be on the GPU")
+    workspace_bytes = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H, D, workspace,
+                                workspace_bytes)
     _check(lib().causal_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), B, S, H, D, float(scale),
                                  _ptr(workspace), int(workspace_bytes), _stream_handle(q, stream)),
            "causal_attn_bwd")
 
 
-def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size,
-                     scale, workspace, workspace_bytes=None, stream=None):
-    """One backward kernel (0: dQ, also writing -delta and lse2; 1: dK/dV); n is S in causal mode."""
-    T = 2 * n if mode == MODE_DIFFUSION else n
-    shp = (B, T, H, D)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
-                    ("dq", dq), ("dk", dk), ("dv", dv)):
-        _want(t, name, torch.bfloat16, shp)
-    _want(lse, "lse", torch.float32, (B, H, T))
+def _want_fwd(q, k, v, out, lse, B, T, H, H_kv, D):
+    bf = torch.bfloat16
+    _want(("q", q, bf, (B, T, H, D)), ("k", k, bf, (B, T, H_kv, D)), ("v", v, bf, (B, T, H_kv, D)),
+          ("out", out, bf, (B, T, H, D)), ("lse", lse, torch.float32, (B, H, T)))
+
+
+def _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace, workspace_bytes):
+    """Check the backward's tensors; returns the workspace size in bytes."""
+    bf = torch.bfloat16
+    qs, kvs = (B, T, H, D), (B, T, H_kv, D)
+    _want(("q", q, bf, qs), ("k", k, bf, kvs), ("v", v, bf, kvs), ("out", out, bf, qs),
+          ("dout", dout, bf, qs), ("lse", lse, torch.float32, (B, H, T)), ("dq", dq, bf, qs),
+          ("dk", dk, bf, kvs), ("dv", dv, bf, kvs))
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a tensor on the GPU")
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    if workspace.device.type != "cuda":
-        raise ValueError("workspace must be on the GPU")
+    return int(workspace_bytes)
+
+
+def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
+                     block_size, scale, workspace, workspace_bytes=None, stream=None):
+    """One backward kernel (0: dQ, also writing -delta and lse2; 1: dK/dV); n is S in causal mode."""
+    T = 2 * n if mode == MODE_DIFFUSION else n
+    wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace, workspace_bytes)
     _check(lib().bdattn_bwd_stage(mode, stage, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, D, block_size,
-                                  float(scale), _ptr(workspace), int(workspace_bytes),
+                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, H_kv, D,
+                                  block_size, float(scale), _ptr(workspace), wsb,
                                   _stream_handle(q, stream)),
            "bdattn_bwd_stage")
+
+
+# Grouped-query attention: q / out / dout / dq carry H heads, k / v / dk / dv
+# carry H_kv (H a multiple of H_kv); query head h reads key/value head
+# h // (H // H_kv).
+
+def diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, H_kv, D, block_size, scale, stream=None):
+    _want_fwd(q, k, v, out, lse, B, 2 * n, H, H_kv, D)
+    _check(lib().diffusion_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, n, H,
+                                        H_kv, D, block_size, float(scale),
+                                        _stream_handle(q, stream)),
+           "diffusion_attn_fwd_gqa")
+
+
+def diffusion_attn_bwd_gqa_workspace_size(B, n, H, H_kv, D) -> int:
+    return int(lib().diffusion_attn_bwd_gqa_workspace_size(B, n, H, H_kv, D))
+
+
+def causal_attn_bwd_gqa_workspace_size(B, S, H, H_kv, D) -> int:
+    return int(lib().causal_attn_bwd_gqa_workspace_size(B, S, H, H_kv, D))
+
+
+def diffusion_attn_bwd_gqa(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D, block_size,
+                           scale, workspace, workspace_bytes=None, stream=None):
+    wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, 2 * n, H, H_kv, D, workspace,
+                    workspace_bytes)
+    _check(lib().diffusion_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, H_kv, D,
+                                        block_size, float(scale), _ptr(workspace), wsb,
+                                        _stream_handle(q, stream)),
+           "diffusion_attn_bwd_gqa")
+
+
+def causal_attn_fwd_gqa(q, k, v, out, lse, B, S, H, H_kv, D, scale, stream=None):
+    _want_fwd(q, k, v, out, lse, B, S, H, H_kv, D)
+    _check(lib().causal_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S, H,
+                                     H_kv, D, float(scale), _stream_handle(q, stream)),
+           "causal_attn_fwd_gqa")
+
+
+def causal_attn_bwd_gqa(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H_kv, D, scale, workspace,
+                        workspace_bytes=None, stream=None):
+    wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H_kv, D, workspace,
+                    workspace_bytes)
+    _check(lib().causal_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), B, S, H, H_kv, D, float(scale),
+                                     _ptr(workspace), wsb, _stream_handle(q, stream)),
+           "causal_attn_bwd_gqa")
 
 
 # ---------------------------------------------------------------------------

@@ -4,7 +4,9 @@
 (batch, 2n, heads, headdim) laid out [noisy | clean] (Fast Diffusion
 Attention, "TL;DR": the same call shape as flash-attention's function, with
 a block size where the causal flag would be) and returns the attention
-output; its backward runs the library's backward kernels.  PyTorch only
+output; its backward runs the library's backward kernels.  k and v may
+carry fewer heads than q (grouped-query attention: H a multiple of H_kv,
+query head h reading key/value head h // (H // H_kv)).  PyTorch only
 allocates the outputs and the workspace and supplies the stream.
 """
 from __future__ import annotations
@@ -25,12 +27,16 @@ class _DiffusionAttn(torch.autograd.Function):
     def forward(ctx, q, k, v, block_size, scale):
         q, k, v = _prep(q), _prep(k), _prep(v)
         B, T, H, D = q.shape
+        Hkv = k.shape[2]
         if T % 2:
             raise ValueError("the sequence length must be 2n ([noisy | clean])")
         n = T // 2
         out = torch.empty_like(q)
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-        _b.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, block_size, scale)
+        if Hkv == H:
+            _b.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, block_size, scale)
+        else:
+            _b.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, block_size, scale)
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.block_size, ctx.scale = block_size, scale
         ctx.mark_non_differentiable(lse)
@@ -41,12 +47,17 @@ class _DiffusionAttn(torch.autograd.Function):
         q, k, v, out, lse = ctx.saved_tensors
         dout = _prep(dout)
         B, T, H, D = q.shape
+        Hkv = k.shape[2]
         n = T // 2
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws_bytes = _b.diffusion_attn_bwd_workspace_size(B, n, H, D)
+        ws_bytes = _b.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        _b.diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, ctx.block_size,
-                              ctx.scale, ws, ws_bytes)
+        if Hkv == H:
+            _b.diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, ctx.block_size,
+                                  ctx.scale, ws, ws_bytes)
+        else:
+            _b.diffusion_attn_bwd_gqa(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, Hkv, D,
+                                      ctx.block_size, ctx.scale, ws, ws_bytes)
         return dq, dk, dv, None, None
 
 
@@ -55,9 +66,13 @@ class _CausalAttn(torch.autograd.Function):
     def forward(ctx, q, k, v, scale):
         q, k, v = _prep(q), _prep(k), _prep(v)
         B, S, H, D = q.shape
+        Hkv = k.shape[2]
         out = torch.empty_like(q)
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-        _b.causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale)
+        if Hkv == H:
+            _b.causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale)
+        else:
+            _b.causal_attn_fwd_gqa(q, k, v, out, lse, B, S, H, Hkv, D, scale)
         ctx.save_for_backward(q, k, v, out, lse)
         ctx.scale = scale
         ctx.mark_non_differentiable(lse)
@@ -68,22 +83,29 @@ class _CausalAttn(torch.autograd.Function):
         q, k, v, out, lse = ctx.saved_tensors
         dout = _prep(dout)
         B, S, H, D = q.shape
+        Hkv = k.shape[2]
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws_bytes = _b.causal_attn_bwd_workspace_size(B, S, H, D)
+        ws_bytes = _b.causal_attn_bwd_gqa_workspace_size(B, S, H, Hkv, D)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        _b.causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, ctx.scale, ws, ws_bytes)
+        if Hkv == H:
+            _b.causal_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, ctx.scale, ws, ws_bytes)
+        else:
+            _b.causal_attn_bwd_gqa(q, k, v, out, dout, lse, dq, dk, dv, B, S, H, Hkv, D, ctx.scale, ws,
+                                   ws_bytes)
         return dq, dk, dv, None
 
 
 def diffusion_attn_func(q, k, v, block_size: int, softmax_scale=None, return_lse: bool = False):
-    """Block-diffusion attention; q, k, v: (batch, 2n, heads, headdim) bf16."""
+    """Block-diffusion attention; q: (batch, 2n, heads, headdim) bf16, k and v:
+    (batch, 2n, kv_heads, headdim) with heads a multiple of kv_heads."""
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     out, lse = _DiffusionAttn.apply(q, k, v, int(block_size), scale)
     return (out, lse) if return_lse else out
 
 
 def causal_attn_func(q, k, v, softmax_scale=None, return_lse: bool = False):
-    """Causal attention (the yardstick); q, k, v: (batch, seq, heads, headdim) bf16."""
+    """Causal attention (the yardstick); q: (batch, seq, heads, headdim) bf16, k
+    and v: (batch, seq, kv_heads, headdim)."""
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     out, lse = _CausalAttn.apply(q, k, v, scale)
     return (out, lse) if return_lse else out

@@ -38,10 +38,17 @@ int check_scale(float scale) {
   return (std::isfinite(scale) && scale != 0.f) ? BDATTN_OK : BDATTN_ERR_INVALID;
 }
 
-bd::AttnArgs make_args(int mode, int B, int n, int H, int b, float scale) {
+// Grouped heads: 1 <= H_kv <= H and H a multiple of H_kv.
+int check_kv_heads(int H, int H_kv) {
+  return (H_kv >= 1 && H_kv <= H && H % H_kv == 0) ? BDATTN_OK : BDATTN_ERR_INVALID;
+}
+
+bd::AttnArgs make_args(int mode, int B, int n, int H, int H_kv, int b, float scale) {
   bd::AttnArgs a{};
   a.B = B;
   a.H = H;
+  a.Hkv = H_kv;
+  a.G = H / H_kv;
   a.n = n;
   a.b = (mode == bd::MODE_CAUSAL) ? 1 : b;
   a.mode = mode;
@@ -53,7 +60,7 @@ bd::AttnArgs make_args(int mode, int B, int n, int H, int b, float scale) {
 }
 
 int fwd_common(int mode, const void* q, const void* k, const void* v, void* out, float* lse,
-               int B, int n, int H, int D, int b, float scale, void* stream) {
+               int B, int n, int H, int H_kv, int D, int b, float scale, void* stream) {
   if (!q || !k || !v || !out || !lse) return BDATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return BDATTN_ERR_INVALID;
@@ -61,8 +68,9 @@ int fwd_common(int mode, const void* q, const void* k, const void* v, void* out,
   if (mode == bd::MODE_DIFFUSION && n > std::numeric_limits<int>::max() / 2) return BDATTN_ERR_INVALID;
   int st = check_shape(B, mode == bd::MODE_CAUSAL ? n : 2 * n, H, D);
   if (st != BDATTN_OK) return st;
+  if ((st = check_kv_heads(H, H_kv)) != BDATTN_OK) return st;
   if ((st = check_scale(scale)) != BDATTN_OK) return st;
-  bd::AttnArgs a = make_args(mode, B, n, H, b, scale);
+  bd::AttnArgs a = make_args(mode, B, n, H, H_kv, b, scale);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -72,15 +80,30 @@ int fwd_common(int mode, const void* q, const void* k, const void* v, void* out,
   return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
 }
 
-size_t workspace_bytes(int B, int T, int H, int D) {
-  if (check_shape(B, T, H, D) != BDATTN_OK) return 0;
-  const size_t bytes = 2 * (size_t)B * H * T * sizeof(float);
-  return (bytes + 255) / 256 * 256;
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Backward workspace: -delta and lse2 per query row ([B][H][T] float32
+// each), then, when the dK/dV kernel splits the groups of query heads
+// (S > 1), float32 partial dK and dV ([S][B][T][H_kv][D] each).
+size_t stats_bytes(int B, int T, int H) { return round256(2 * (size_t)B * H * T * sizeof(float)); }
+
+int splits_of(int mode, int B, int n, int H, int H_kv) {
+  return bd::dkdv_group_splits(B, n, mode == bd::MODE_CAUSAL ? 1 : 2, H_kv, H / H_kv);
+}
+
+size_t workspace_bytes(int mode, int B, int n, int H, int H_kv, int D) {
+  if (n < 1 || (mode == bd::MODE_DIFFUSION && n > std::numeric_limits<int>::max() / 2)) return 0;
+  const int T = (mode == bd::MODE_CAUSAL) ? n : 2 * n;
+  if (check_shape(B, T, H, D) != BDATTN_OK || check_kv_heads(H, H_kv) != BDATTN_OK) return 0;
+  const int S = splits_of(mode, B, n, H, H_kv);
+  const size_t part = S > 1 ? 2 * (size_t)S * B * T * H_kv * D * sizeof(float) : 0;
+  return stats_bytes(B, T, H) + round256(part);
 }
 
 int bwd_common(int mode, int stage, const void* q, const void* k, const void* v, const void* out,
                const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int n,
-               int H, int D, int b, float scale, void* workspace, size_t ws_bytes, void* stream) {
+               int H, int H_kv, int D, int b, float scale, void* workspace, size_t ws_bytes,
+               void* stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
     return BDATTN_ERR_INVALID;
   const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
@@ -91,9 +114,11 @@ int bwd_common(int mode, int stage, const void* q, const void* k, const void* v,
   const int T = (mode == bd::MODE_CAUSAL) ? n : 2 * n;
   int st = check_shape(B, T, H, D);
   if (st != BDATTN_OK) return st;
+  if ((st = check_kv_heads(H, H_kv)) != BDATTN_OK) return st;
   if ((st = check_scale(scale)) != BDATTN_OK) return st;
-  if (ws_bytes < workspace_bytes(B, T, H, D)) return BDATTN_ERR_INVALID;
-  bd::AttnArgs a = make_args(mode, B, n, H, b, scale);
+  if (ws_bytes < workspace_bytes(mode, B, n, H, H_kv, D)) return BDATTN_ERR_INVALID;
+  bd::AttnArgs a = make_args(mode, B, n, H, H_kv, b, scale);
+  a.S = splits_of(mode, B, n, H, H_kv);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -102,6 +127,8 @@ int bwd_common(int mode, int stage, const void* q, const void* k, const void* v,
   a.lse_in = lse;
   a.ndelta = static_cast<float*>(workspace);
   a.lse2 = a.ndelta + (size_t)B * H * T;
+  a.part = a.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(B, T, H))
+                   : nullptr;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
@@ -130,46 +157,82 @@ const char* bdattn_status_string(int status) {
 
 int diffusion_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                        int n, int H, int D, int block_size, float scale, void* stream) {
-  return fwd_common(bd::MODE_DIFFUSION, q, k, v, out, lse, B, n, H, D, block_size, scale, stream);
+  return fwd_common(bd::MODE_DIFFUSION, q, k, v, out, lse, B, n, H, H, D, block_size, scale,
+                    stream);
+}
+
+int diffusion_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* stream) {
+  return fwd_common(bd::MODE_DIFFUSION, q, k, v, out, lse, B, n, H, H_kv, D, block_size, scale,
+                    stream);
 }
 
 size_t diffusion_attn_bwd_workspace_size(int B, int n, int H, int D) {
-  if (n < 1 || n > std::numeric_limits<int>::max() / 2) return 0;
-  return workspace_bytes(B, 2 * n, H, D);
+  return workspace_bytes(bd::MODE_DIFFUSION, B, n, H, H, D);
+}
+
+size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D) {
+  return workspace_bytes(bd::MODE_DIFFUSION, B, n, H, H_kv, D);
 }
 
 int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                        int n, int H, int D, int block_size, float scale, void* workspace,
                        size_t workspace_bytes_, void* stream) {
-  return bwd_common(bd::MODE_DIFFUSION, -1, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D,
+  return bwd_common(bd::MODE_DIFFUSION, -1, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H, D,
+                    block_size, scale, workspace, workspace_bytes_, stream);
+}
+
+int diffusion_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                           int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* workspace, size_t workspace_bytes_, void* stream) {
+  return bwd_common(bd::MODE_DIFFUSION, -1, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
                     block_size, scale, workspace, workspace_bytes_, stream);
 }
 
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                     int S, int H, int D, float scale, void* stream) {
-  return fwd_common(bd::MODE_CAUSAL, q, k, v, out, lse, B, S, H, D, 1, scale, stream);
+  return fwd_common(bd::MODE_CAUSAL, q, k, v, out, lse, B, S, H, H, D, 1, scale, stream);
+}
+
+int causal_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                        int S, int H, int H_kv, int D, float scale, void* stream) {
+  return fwd_common(bd::MODE_CAUSAL, q, k, v, out, lse, B, S, H, H_kv, D, 1, scale, stream);
 }
 
 size_t causal_attn_bwd_workspace_size(int B, int S, int H, int D) {
-  return workspace_bytes(B, S, H, D);
+  return workspace_bytes(bd::MODE_CAUSAL, B, S, H, H, D);
+}
+
+size_t causal_attn_bwd_gqa_workspace_size(int B, int S, int H, int H_kv, int D) {
+  return workspace_bytes(bd::MODE_CAUSAL, B, S, H, H_kv, D);
 }
 
 int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int S,
                     int H, int D, float scale, void* workspace, size_t workspace_bytes_,
                     void* stream) {
-  return bwd_common(bd::MODE_CAUSAL, -1, q, k, v, out, dout, lse, dq, dk, dv, B, S, H, D, 1, scale,
-                    workspace, workspace_bytes_, stream);
+  return bwd_common(bd::MODE_CAUSAL, -1, q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H, D, 1,
+                    scale, workspace, workspace_bytes_, stream);
+}
+
+int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int S, int H, int H_kv, int D, float scale, void* workspace,
+                        size_t workspace_bytes_, void* stream) {
+  return bwd_common(bd::MODE_CAUSAL, -1, q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H_kv, D, 1,
+                    scale, workspace, workspace_bytes_, stream);
 }
 
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
-                     void* dv, int B, int n, int H, int D, int block_size, float scale,
+                     void* dv, int B, int n, int H, int H_kv, int D, int block_size, float scale,
                      void* workspace, size_t workspace_bytes_, void* stream) {
   if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
   if (stage < 0 || stage > 1) return BDATTN_ERR_INVALID;
-  return bwd_common(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D,
+  return bwd_common(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
                     mode == bd::MODE_CAUSAL ? 1 : block_size, scale, workspace, workspace_bytes_,
                     stream);
 }

@@ -5,9 +5,13 @@
 //          stores -delta and lse2 (float32) in the caller's workspace; then
 //          it walks the key tiles its rows see and accumulates
 //          dQ = scale * dS K;
-//   dkdv : one workgroup per 128-key tile (runs after dq, reading the
-//          workspace); it walks the query tiles that see its keys and
-//          accumulates dV = P^T dO and dK = scale * dS^T Q in registers.
+//   dkdv : one workgroup per 128-key tile of one key/value head (runs
+//          after dq, reading the workspace); it walks the query tiles that
+//          see its keys, for every query head that reads the key/value head
+//          in turn, and accumulates dV = P^T dO and dK = scale * dS^T Q in
+//          registers.  With grouped query heads the key tile is loaded once
+//          for the whole group and the group's sum needs no atomics (Fast
+//          Diffusion Attention, "Ampere and Ada": the GQA-grouped backward).
 //
 // FlashAttention: Exact Attention Without Materialization, section 4.5:
 // the probabilities are recomputed on chip from Q, K and the saved
@@ -52,7 +56,7 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
 // selects: grouped in a struct, the compiler would select between the
 // structs' addresses and keep both in scratch memory.
 #define COL_SEGMENTS                                                          \
-  const size_t stat_base = ((size_t)bi * a.H + hh) * a.T;                    \
+  const size_t stat_base = ((size_t)bi * a.H + hh0) * a.T;                   \
   int clo_f0, chi_f0, clo_l0, chi_l0, clo_p0, chi_p0;                        \
   int clo_f1, chi_f1, clo_l1, chi_l1, clo_p1, chi_p1;                        \
   col_interval(g, seg.half0, kh, kw0, clo_f0, chi_f0);                        \
@@ -61,8 +65,8 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
   col_interval(g, seg.half1, kh, kw0, clo_f1, chi_f1);                        \
   col_interval(g, seg.half1, kh, max(kw1 - 1, kw0), clo_l1, chi_l1);          \
   col_interval(g, seg.half1, kh, key, clo_p1, chi_p1);                        \
-  const size_t qb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh * D; \
-  const size_t qb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh * D; \
+  const size_t qb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh0 * D; \
+  const size_t qb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh0 * D; \
   const size_t sb0 = stat_base + half_off(a, seg.half0);                      \
   const size_t sb1 = stat_base + half_off(a, seg.half1);
 
@@ -74,8 +78,8 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
   row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);                            \
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);              \
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);                              \
-  const size_t kvb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh * D;  \
-  const size_t kvb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh * D;
+  const size_t kvb0 = (sample0 + half_off(a, seg.half0)) * rs_kv + (size_t)hk * D; \
+  const size_t kvb1 = (sample0 + half_off(a, seg.half1)) * rs_kv + (size_t)hk * D;
 
 // ---------------------------------------------------------------------------
 // dK / dV: key-stationary, one workgroup per 128 keys, 8 waves in 4 pairs.
@@ -108,7 +112,10 @@ struct DkdvCfg {
   static constexpr int PXS = NPAIR * QB * 2 * 64;  // 16-byte slots of one P exchange buffer
 };
 
-template <int D>
+// GROUPED: G > 1 query heads per key/value head (the walk spans several
+// query heads, and with S > 1 the workgroup writes float32 partials); the
+// plain multi-head instance compiles none of that.
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
   using C = DkdvCfg<D>;
   using Tile = typename C::Tile;
@@ -126,7 +133,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  const int BH = a.B * a.H;
+  // One workgroup per (key tile, sample, key/value head, split); it walks
+  // the query tiles of the G / S query heads of its split of the group (the
+  // grouped backward: the key tile is loaded once for all of them).
+  const int S = GROUPED ? a.S : 1;
+  const int BH = a.B * a.Hkv * S;
   const int bid = blockIdx.x;
   int kh, kt, bh;
   if (bid < ktiles * BH) {
@@ -138,13 +149,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     kt = (bid - ktiles * BH) / BH;
     bh = (bid - ktiles * BH) % BH;
   }
-  const int bi = bh / a.H;
-  const int hh = bh % a.H;
+  const int split = GROUPED ? bh % S : 0;
+  const int bi = bh / S / a.Hkv;
+  const int hk = bh / S % a.Hkv;
+  const int gs = GROUPED ? a.G / S : 1;         // query heads walked by this workgroup
+  const int hh0 = GROUPED ? hk * a.G + split * gs : hk;  // the first of them
   const Geom g{a.n, a.b};
+  // Q / dO rows hold H heads, K / V / dK / dV rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
+  const size_t rs_kv = (size_t)a.Hkv * D;
   const size_t sample0 = (size_t)bi * a.T;
   const uint32_t row_bytes = (uint32_t)rs * 2u;
   const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
   const size_t koff = sample0 + half_off(a, kh);
 
   const int kw0 = kt * C::BKV + 32 * pair;  // the pair's first key
@@ -155,10 +172,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   // The P-wave holds K, the dS-wave V, as B operands.
   bf16x8 xf[C::KS];
   {
-    const rsrc_t rx = make_rsrc((pwave ? a.k : a.v) + koff * rs + (size_t)hh * D, half_bytes);
+    const rsrc_t rx = make_rsrc((pwave ? a.k : a.v) + koff * rs_kv + (size_t)hk * D,
+                                (uint32_t)a.n * kv_row_bytes);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
-      xf[s] = as_bf16x8(buf_ld16(rx, (uint32_t)key * row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0));
+      xf[s] = as_bf16x8(buf_ld16(rx, (uint32_t)key * kv_row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0));
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) settle(xf[s]);
   }
@@ -166,12 +184,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const Segments seg = bwd_segments(g, a.mode, kh, kt, C::BQ, C::BKV);
   const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
   const int ntiles = seg.tiles();
+  // Step t of the walk is tile t mod ntiles of query head hh0 + t / ntiles.
+  const int nsteps = gs * ntiles;
+  auto head_of_step = [&](int t) -> int { return (!GROUPED || gs == 1) ? 0 : t / ntiles; };
   COL_SEGMENTS
-  auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const int gi = head_of_step(t);
+    const int i = t - gi * ntiles;
     const bool second = i >= n0;
     const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-    const size_t qb = second ? qb1 : qb0;
-    const size_t sb = second ? sb1 : sb0;
+    const size_t qb = (second ? qb1 : qb0) + (size_t)gi * D;
+    const size_t sb = (second ? sb1 : sb0) + (size_t)gi * a.T;
     const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
     Tile::load(make_rsrc(a.q + qb, half_bytes), row_bytes, qt * C::BQ, dst, tid);
     Tile::load(make_rsrc(a.dout + qb, half_bytes), row_bytes, qt * C::BQ, dst + Tile::ELEMS * 2u, tid);
@@ -190,13 +213,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) acc[i] = zero16();
 
-  if (pwave && ntiles > 0) issue_tile(0, 0);
+  if (pwave && nsteps > 0) issue_tile(0, 0);
   wait_vmem();
   __syncthreads();
 
   // The two roles run separate copies of the walk, so that each is
   // register-allocated for its own state only.  Both pass one workgroup
-  // barrier per step, ntiles + 1 steps.  In step j the P-wave computes S, P
+  // barrier per step, nsteps + 1 steps.  In step j the P-wave computes S, P
   // and dV for tile j (products, elementwise, products); the dS-wave first
   // finishes tile j - 1 (dS from the dP it computed in the previous step,
   // then dK) and then computes dP for tile j.  The two waves of a pair share
@@ -224,8 +247,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 
     // Which 32-row blocks of tile i see some key of the pair (act) or every
     // key of it (full); qt, and the rows [clo, chi) that see this lane's key.
-    auto blocks = [&](int i, bool (&act)[C::QB], bool (&full)[C::QB], int& qt, int& clo, int& chi)
+    auto blocks = [&](int t, bool (&act)[C::QB], bool (&full)[C::QB], int& qt, int& clo, int& chi)
         __attribute__((always_inline)) {
+      const int i = t - head_of_step(t) * ntiles;
       const bool second = i >= n0;
       qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
       const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
@@ -305,9 +329,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
       constexpr int slot = decltype(slotc)::value;
       constexpr int slot_next = (slot + 1) % C::NBUF;
       constexpr int slot_prev = (slot + C::NBUF - 1) % C::NBUF;
-      if (PW && j + 1 < ntiles) issue_tile(j + 1, slot_next);
+      if (PW && j + 1 < nsteps) issue_tile(j + 1, slot_next);
       if constexpr (PW) {
-        if (j < ntiles) {
+        if (j < nsteps) {
           const uint16_t* Tb = smem + slot * C::BUF;
           const float* Ls = fsm + slot * C::FBUF;
           u32x4* px = pex + (j & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
           step(Q0{});
           step(Q1{});
         }
-        if (j < ntiles) {
+        if (j < nsteps) {
           bool full[C::QB];
           int qt, clo, chi;
           blocks(j, pact, full, qt, clo, chi);
@@ -400,10 +424,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
       __syncthreads();
     };
     static_assert(C::NBUF == 3, "the step loop is unrolled by the ring depth");
-    for (int j0 = 0; j0 <= ntiles; j0 += C::NBUF) {
+    for (int j0 = 0; j0 <= nsteps; j0 += C::NBUF) {
       step_j(std::integral_constant<int, 0>{}, j0);
-      if (j0 + 1 <= ntiles) step_j(std::integral_constant<int, 1>{}, j0 + 1);
-      if (j0 + 2 <= ntiles) step_j(std::integral_constant<int, 2>{}, j0 + 2);
+      if (j0 + 1 <= nsteps) step_j(std::integral_constant<int, 1>{}, j0 + 1);
+      if (j0 + 2 <= nsteps) step_j(std::integral_constant<int, 2>{}, j0 + 2);
     }
   };
   if (pwave)
@@ -413,19 +437,59 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 
   // lane = key, register r of block db = dimension 32db + 8(r/4) + 4h2 + r%4
   if (pair_active && key < a.n) {
-    const size_t off = (koff + key) * rs + (size_t)hh * D;
-    uint16_t* dst = (pwave ? a.dv : a.dk) + off;
+    const size_t off = (koff + key) * rs_kv + (size_t)hk * D;
     const float f = pwave ? 1.f : a.scale;
+    if (S == 1) {
+      uint16_t* dst = (pwave ? a.dv : a.dk) + off;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * h2;
-        u32x2 pk = {pack2_bf16(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
-                    pack2_bf16(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
-        *reinterpret_cast<u32x2*>(dst + d) = pk;
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * h2;
+          u32x2 pk = {pack2_bf16(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
+                      pack2_bf16(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
+          *reinterpret_cast<u32x2*>(dst + d) = pk;
+        }
+    } else {
+      // float32 partial of this split: [S][B][T][Hkv][D], dK then dV
+      const size_t E = (size_t)a.B * a.T * a.Hkv * D;
+      float* dst = a.part + (pwave ? (size_t)S * E : 0) + (size_t)split * E + off;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * h2;
+          float4 x = {acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f, acc[db][4 * gq + 2] * f,
+                      acc[db][4 * gq + 3] * f};
+          *reinterpret_cast<float4*>(dst + d) = x;
+        }
+    }
   }
+}
+
+// dK and dV of split groups: the sum of the S float32 partials, in split
+// order, rounded to bf16.  Each thread produces 8 consecutive elements of
+// the [B][T][Hkv][D] outputs; elements [0, E) are dK, [E, 2E) dV.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
+                                                         uint16_t* __restrict__ dk,
+                                                         uint16_t* __restrict__ dv, long long E,
+                                                         int S) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= 2 * E) return;
+  const bool second = i >= E;
+  const long long e = second ? i - E : i;
+  const float* src = part + (second ? (long long)S * E : 0) + e;
+  float4 lo = *reinterpret_cast<const float4*>(src);
+  float4 hi = *reinterpret_cast<const float4*>(src + 4);
+  for (int s = 1; s < S; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (long long)s * E);
+    const float4 y = *reinterpret_cast<const float4*>(src + (long long)s * E + 4);
+    lo.x += x.x; lo.y += x.y; lo.z += x.z; lo.w += x.w;
+    hi.x += y.x; hi.y += y.y; hi.z += y.z; hi.w += y.w;
+  }
+  const u32x4 pk = {pack2_bf16(lo.x, lo.y), pack2_bf16(lo.z, lo.w), pack2_bf16(hi.x, hi.y),
+                    pack2_bf16(hi.z, hi.w)};
+  *reinterpret_cast<u32x4*>((second ? dv : dk) + e) = pk;
 }
 
 // ---------------------------------------------------------------------------
@@ -464,16 +528,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   const int qt = qtiles - 1 - bid / R;
   const int rr = bid % R;
   const int half_idx = rr / BH;
-  const int bh = rr % BH;
-  const int bi = bh / a.H;
-  const int hh = bh % a.H;
+  int bi, hh, hk;
+  query_head(a, rr % BH, bi, hh, hk);
   const int qh = (a.mode == MODE_CAUSAL) ? CLEAN : half_idx;
   const Geom g{a.n, a.b};
+  // Q / dO / O / dQ rows hold H heads, K / V rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
+  const size_t rs_kv = (size_t)a.Hkv * D;
   const size_t sample0 = (size_t)bi * a.T;
   const int qoff = half_off(a, qh);
   const uint32_t row_bytes = (uint32_t)rs * 2u;
   const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
+  const uint32_t kv_half_bytes = (uint32_t)a.n * kv_row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
@@ -542,8 +609,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
     const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
     const size_t kvb = second ? kvb1 : kvb0;
     const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
-    Tile::load(make_rsrc(a.k + kvb, half_bytes), row_bytes, kt * BN, dst, tid);
-    Tile::load(make_rsrc(a.v + kvb, half_bytes), row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
+    Tile::load(make_rsrc(a.k + kvb, kv_half_bytes), kv_row_bytes, kt * BN, dst, tid);
+    Tile::load(make_rsrc(a.v + kvb, kv_half_bytes), kv_row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
   };
 
   floatx16 dq[C::DB];
@@ -663,10 +730,36 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
   } else {
     using KC = DkdvCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
-    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.Hkv * a.S;
+    if (a.G > 1)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+    if (a.S > 1) {
+      const long long E = (long long)a.B * a.T * a.Hkv * D;
+      const long long rblocks = (2 * E / 8 + 255) / 256;
+      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, s, a.part, a.dk,
+                         a.dv, E, a.S);
+    }
   }
   return hipGetLastError();
+}
+
+// Fewer dK/dV workgroups than this leave CUs idle or the tail unbalanced
+// (4 per CU on 256 CUs).
+constexpr long long kDkdvMinBlocks = 1024;
+
+int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G) {
+  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV, "one key tile size for both widths");
+  const long long ktiles = ((long long)n + DkdvCfg<128>::BKV - 1) / DkdvCfg<128>::BKV;
+  const long long base = ktiles * nhalves * B * Hkv;
+  int S = 1;
+  for (int c = 1; c <= G; ++c) {
+    if (G % c) continue;
+    S = c;
+    if (base * c >= kDkdvMinBlocks) break;
+  }
+  return S;
 }
 
 hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s) {

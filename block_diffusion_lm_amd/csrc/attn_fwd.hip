@@ -71,24 +71,28 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
 
   // Heaviest query tiles first; within one tile index, both halves of a
   // (sample, head) sit at the same residue modulo the XCD count when B*H is
-  // a multiple of 8, so they share an L2.
+  // a multiple of 8, so they share an L2 (and so do the query heads of one
+  // key/value head, see query_head).
   const int BH = a.B * a.H;
   const int R = a.nhalves * BH;
   const int bid = blockIdx.x;
   const int qt = qtiles - 1 - bid / R;
   const int rr = bid % R;
   const int half_idx = rr / BH;
-  const int bh = rr % BH;
-  const int bi = bh / a.H;
-  const int hh = bh % a.H;
+  int bi, hh, hk;
+  query_head(a, rr % BH, bi, hh, hk);
   const int qh = (a.mode == MODE_CAUSAL) ? CLEAN : half_idx;
   const Geom g{a.n, a.b};
 
+  // Q / O rows hold H heads, K / V rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
+  const size_t rs_kv = (size_t)a.Hkv * D;
   const size_t sample0 = (size_t)bi * a.T;
   const int qoff = half_offset(a, qh);
   const uint32_t row_bytes = (uint32_t)rs * 2u;
   const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
+  const uint32_t kv_half_bytes = (uint32_t)a.n * kv_row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
@@ -130,16 +134,16 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
   row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);
-  const size_t kvb0 = (sample0 + half_offset(a, seg.half0)) * rs + (size_t)hh * D;
-  const size_t kvb1 = (sample0 + half_offset(a, seg.half1)) * rs + (size_t)hh * D;
+  const size_t kvb0 = (sample0 + half_offset(a, seg.half0)) * rs_kv + (size_t)hk * D;
+  const size_t kvb1 = (sample0 + half_offset(a, seg.half1)) * rs_kv + (size_t)hk * D;
 
   auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
     const bool second = i >= n0;
     const int kt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
     const size_t kvb = second ? kvb1 : kvb0;
     const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
-    Tile::load(make_rsrc(a.k + kvb, half_bytes), row_bytes, kt * BN, dst, tid);
-    Tile::load(make_rsrc(a.v + kvb, half_bytes), row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
+    Tile::load(make_rsrc(a.k + kvb, kv_half_bytes), kv_row_bytes, kt * BN, dst, tid);
+    Tile::load(make_rsrc(a.v + kvb, kv_half_bytes), kv_row_bytes, kt * BN, dst + Tile::ELEMS * 2u, tid);
   };
 
   floatx16 o[C::DB];

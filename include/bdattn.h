@@ -98,20 +98,22 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One stage of the backward pass (same arguments as diffusion_attn_bwd /
- * causal_attn_bwd; mode 0 = diffusion with block_size, 1 = causal with n = S
- * and block_size ignored):
+ * One stage of the backward pass (same arguments as diffusion_attn_bwd_gqa and
+ * causal_attn_bwd_gqa below, with their workspace; H_kv = H for plain
+ * multi-head attention; mode 0 = diffusion with block_size, 1 = causal with
+ * n = S and block_size ignored):
  *   stage 0 -- dQ; it also writes the per-row -delta_i = -(dout_i . out_i)
  *              and lse_i * log2(e) to the workspace;
- *   stage 1 -- dK and dV (reads the workspace written by stage 0).
+ *   stage 1 -- dK and dV (reads the workspace written by stage 0; with
+ *              split groups also the reduction of the partials).
  * The full backward is stages 0 and 1, in that order, on one stream (or
  * with stage 1 ordered after stage 0).  Other stage numbers return
  * BDATTN_ERR_INVALID.
  */
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
-                     void* dv, int B, int n, int H, int D, int block_size, float scale,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     void* dv, int B, int n, int H, int H_kv, int D, int block_size,
+                     float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal yardstick forward: q, k, v, out [B][S][H][D] bf16, lse [B][H][S] fp32. */
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -125,6 +127,47 @@ int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
                     int B, int S, int H, int D, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped-query attention (GQA; multi-query attention when H_kv = 1): the H
+ * query heads share H_kv key/value heads.  Query heads form H_kv consecutive
+ * groups of H / H_kv; query head h reads key/value head h / (H / H_kv).
+ *   q, out, dout, dq : [B][T][H][D]    bf16
+ *   k, v, dk, dv     : [B][T][H_kv][D] bf16
+ *   lse              : [B][H][T]       fp32 (one per query row, as above)
+ * dk and dv of a key/value head are the sums of the gradients that its
+ * query heads send it.  The dK/dV kernel walks all query heads of a group
+ * for each key tile, so that tile is loaded once for the group and the sum
+ * is formed in registers, without atomics (Fast Diffusion Attention,
+ * "Ampere and Ada": the GQA-grouped backward).  Requires 1 <= H_kv <= H and
+ * H a multiple of H_kv (BDATTN_ERR_INVALID otherwise).  With H_kv = H
+ * these compute exactly what the plain entry points compute.
+ *
+ * When one workgroup per (key tile, sample, key/value head) would leave the
+ * GPU short of work (few samples, key/value heads or key tiles), each group
+ * is split over several workgroups that write float32 partial dK / dV to
+ * the workspace, and a reduction adds the partials in a fixed order: the
+ * result is still deterministic.  The *_gqa_workspace_size functions
+ * return the bytes this needs: the per-row statistics of the plain entry
+ * points, plus the partials when the groups are split (at most about
+ * 2 * 1024 * 128 * D * 4 bytes, since groups are split only for small
+ * problems).  They return 0 on bad sizes.
+ */
+size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D);
+size_t causal_attn_bwd_gqa_workspace_size(int B, int S, int H, int H_kv, int D);
+int diffusion_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* stream);
+int diffusion_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int causal_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int S, int H, int H_kv, int D, float scale, void* stream);
+int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int S, int H, int H_kv, int D, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Host-side inspection of the tile enumeration the kernels use (pure integer

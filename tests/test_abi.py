@@ -84,7 +84,7 @@ def test_bwd_rejects(kw, want):
 def test_bwd_stage_rejects_unknown_stage(stage):
     # stage 0 is dQ (with the row statistics), stage 1 dK/dV; nothing else
     lib = bd.lib()
-    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), 1, 16, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
+    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), 1, 16, 1, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
 
 
 def test_causal_rejects():
@@ -107,5 +107,77 @@ def test_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
     lse = torch.zeros(1, 1, 8)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="on the GPU"):
         bd.diffusion_attn_fwd(x, x, x, x.clone(), lse, 1, 4, 1, 64, 2, 0.125)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, -1), (4, 8), (6, 4), (5, 2)])
+def test_grouped_entry_points_reject_bad_kv_heads(H, H_kv):
+    # 1 <= H_kv <= H with H a multiple of H_kv; the rest of each call is valid
+    lib = bd.lib()
+    assert lib.diffusion_attn_fwd_gqa(*([FAKE] * 5), 1, 16, H, H_kv, 64, 4, 0.125, None) == INVALID
+    assert lib.diffusion_attn_bwd_gqa(*([FAKE] * 9), 1, 16, H, H_kv, 64, 4, 0.125, FAKE, 1 << 20,
+                                      None) == INVALID
+    assert lib.causal_attn_fwd_gqa(*([FAKE] * 5), 1, 16, H, H_kv, 64, 0.125, None) == INVALID
+    assert lib.causal_attn_bwd_gqa(*([FAKE] * 9), 1, 16, H, H_kv, 64, 0.125, FAKE, 1 << 20,
+                                   None) == INVALID
+    assert lib.bdattn_bwd_stage(0, 0, *([FAKE] * 9), 1, 16, H, H_kv, 64, 4, 0.125, FAKE, 1 << 20,
+                                None) == INVALID
+
+
+def test_grouped_entry_points_share_the_other_checks():
+    lib = bd.lib()
+    assert lib.diffusion_attn_fwd_gqa(*([FAKE] * 5), 1, 16, 4, 2, 96, 4, 0.125, None) == UNSUPPORTED
+    assert lib.diffusion_attn_fwd_gqa(None, *([FAKE] * 4), 1, 16, 4, 2, 64, 4, 0.125, None) == INVALID
+    assert lib.diffusion_attn_bwd_gqa(*([FAKE] * 9), 1, 16, 4, 2, 64, 4, 0.125, FAKE, 4, None) == INVALID
+
+
+def test_grouped_binding_checks_kv_shapes():
+    import torch
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)  # 4 heads where 2 are expected
+    lse = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError, match=r"k must have shape \(1, 8, 2, 64\)"):
+        bd.diffusion_attn_fwd_gqa(q, kv, kv, q.clone(), lse, 1, 4, 4, 2, 64, 2, 0.125)
+
+
+def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
+    """Statistics (two float32 per query row) plus, when the dK/dV kernel
+    splits the groups, float32 partial dK and dV per split.  The split count
+    is the smallest divisor S of G = H / Hkv giving at least 1024 dK/dV
+    workgroups of 128 keys (all of G when none does)."""
+    T = n if causal else 2 * n
+    r256 = lambda x: -(-x // 256) * 256
+    base = -(-n // 128) * (1 if causal else 2) * B * Hkv
+    G = H // Hkv
+    S = next((c for c in range(1, G + 1) if G % c == 0 and base * c >= 1024), G)
+    part = 2 * S * B * T * Hkv * D * 4 if S > 1 else 0
+    return r256(2 * B * H * T * 4) + r256(part), S
+
+
+@pytest.mark.parametrize("B,n,H,Hkv,D", [
+    (8, 1024, 32, 8, 128),   # 1024 workgroups unsplit: S = 1
+    (4, 2048, 16, 1, 64),    # multi-query, 128 workgroups: S = 8
+    (2, 100, 4, 2, 64),      # tiny: every query head on its own, S = G
+    (1, 7, 8, 2, 128),
+    (3, 5000, 12, 12, 64),   # plain multi-head
+])
+def test_gqa_workspace_sizes(B, n, H, Hkv, D):
+    want, S = _expected_gqa_workspace(B, n, H, Hkv, D)
+    assert bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D) == want
+    wantc, _ = _expected_gqa_workspace(B, n, H, Hkv, D, causal=True)
+    assert bd.causal_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D) == wantc
+    if Hkv == H:
+        assert want == bd.diffusion_attn_bwd_workspace_size(B, n, H, D)
+    assert bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, H + 1, D) == 0
+    assert bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, 0, D) == 0
+
+
+def test_gqa_bwd_rejects_a_workspace_without_room_for_partials():
+    # multi-query at this size splits the groups, so the statistics alone
+    # are not enough workspace
+    B, n, H, D = 4, 2048, 16, 64
+    stats_only = bd.diffusion_attn_bwd_workspace_size(B, n, H, D)
+    assert bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, 1, D) > stats_only
+    assert bd.lib().diffusion_attn_bwd_gqa(*([FAKE] * 9), B, n, H, 1, D, 4, 0.125, FAKE, stats_only,
+                                           None) == INVALID

@@ -26,7 +26,7 @@ import torch
 
 import oracle
 import block_diffusion_lm_amd as bd
-from workloads import WORKLOADS, make_causal_view, make_inputs, make_workload_inputs
+from workloads import GQA_WORKLOADS, WORKLOADS, make_causal_view, make_inputs, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,31 @@ def run_diffusion(q, k, v, do, b, scale, bwd=True):
         bd.diffusion_attn_bwd(q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, b, scale, ws)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
+    return {key: t.cpu() for key, t in res.items()}
+
+
+def run_grouped(q, k, v, do, b, scale, causal=False):
+    """Forward and backward through the grouped-query entry points (k and v
+    carry H_kv heads); returns CPU tensors."""
+    dev = _dev()
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if causal:
+        bd.causal_attn_fwd_gqa(q, k, v, out, lse, B, T, H, Hkv, D, scale)
+        ws = torch.empty(bd.causal_attn_bwd_gqa_workspace_size(B, T, H, Hkv, D), dtype=torch.uint8, device=dev)
+        bd.causal_attn_bwd_gqa(q, k, v, out, do, lse, dq, dk, dv, B, T, H, Hkv, D, scale, ws)
+    else:
+        n = T // 2
+        bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
+        ws = torch.empty(bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D), dtype=torch.uint8,
+                         device=dev)
+        bd.diffusion_attn_bwd_gqa(q, k, v, out, do, lse, dq, dk, dv, B, n, H, Hkv, D, b, scale, ws)
+    torch.cuda.synchronize()
+    res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
     return {key: t.cpu() for key, t in res.items()}
 
 
@@ -253,11 +278,11 @@ def test_backward_stages_in_order_on_two_streams():
     done0 = torch.cuda.Event()
     torch.cuda.synchronize()
     with torch.cuda.stream(s1):
-        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s1)
+        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, H, D, w.b, scale, ws, stream=s1)
         done0.record(s1)
     s2.wait_event(done0)
     with torch.cuda.stream(s2):
-        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, D, w.b, scale, ws, stream=s2)
+        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, H, D, w.b, scale, ws, stream=s2)
     torch.cuda.synchronize()
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(t.cpu(), ref[name]), name
@@ -341,3 +366,135 @@ def test_causal_yardstick_workload():
                                             f(do[si, :, hi]), scale)
         for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV)):
             check_grad(res[name][si, :, hi], ref, name, f"causal c3 seq {si}")
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention (query heads sharing key/value heads)
+# ---------------------------------------------------------------------------
+
+def compare_grouped(res, q, k, v, do, b, scale, what, causal=False, groups=None):
+    """Oracle check of a grouped result; ``groups`` lists (sample, key/value
+    head) pairs to check (default: all), each with all the query heads that
+    read it."""
+    f = oracle.to_f64
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    G = H // Hkv
+    one_fwd = (lambda qq, kk, vv, **kw: oracle.causal_forward(qq, kk, vv, kw["scale"])) if causal \
+        else oracle.diffusion_forward
+    one_bwd = (lambda qq, kk, vv, dd, **kw: oracle.causal_backward(qq, kk, vv, dd, kw["scale"])) if causal \
+        else oracle.diffusion_backward
+    todo = groups if groups is not None else [(bi, j) for bi in range(B) for j in range(Hkv)]
+    for bi, j in todo:
+        hs = slice(j * G, (j + 1) * G)
+        sq, sdo = f(q[bi:bi + 1, :, hs]), f(do[bi:bi + 1, :, hs])
+        sk, sv = f(k[bi:bi + 1, :, j:j + 1]), f(v[bi:bi + 1, :, j:j + 1])
+        O, L = oracle.grouped_forward(one_fwd, sq, sk, sv, b=b, scale=scale)
+        dQ, dK, dV = oracle.grouped_backward(one_bwd, sq, sk, sv, sdo, b=b, scale=scale)
+        tag = f"{what} sample {bi} kv head {j}"
+        check_fwd(res["out"][bi:bi + 1, :, hs], res["lse"][bi:bi + 1, hs], O, L, tag)
+        check_grad(res["dq"][bi:bi + 1, :, hs], dQ, "dq", tag)
+        check_grad(res["dk"][bi:bi + 1, :, j:j + 1], dK, "dk", tag)
+        check_grad(res["dv"][bi:bi + 1, :, j:j + 1], dV, "dv", tag)
+
+
+GQA_SMALL = [  # B, n, H, H_kv, D, b
+    (2, 100, 4, 2, 64, 16), (1, 129, 6, 3, 128, 7), (2, 300, 4, 1, 64, 64),
+    (1, 7, 8, 2, 128, 3), (1, 257, 8, 1, 128, 32), (2, 64, 3, 1, 64, 200),
+]
+
+
+@pytest.mark.parametrize("B,n,H,Hkv,D,b", GQA_SMALL)
+def test_grouped_small(B, n, H, Hkv, D, b):
+    q, k, v, do = make_inputs(B, n, H, D, seed=9300 + n + H + Hkv, H_kv=Hkv)
+    scale = 1 / math.sqrt(D)
+    res = run_grouped(q, k, v, do, b, scale)
+    compare_grouped(res, q, k, v, do, b, scale, f"gqa n{n} H{H}/{Hkv} D{D} b{b}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_grouped_causal_small(D):
+    q, k, v, do = make_inputs(2, 150, 6, D, seed=9400 + D, H_kv=2)
+    q, k, v, do = (x[:, :150].contiguous() for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    res = run_grouped(q, k, v, do, 1, scale, causal=True)
+    compare_grouped(res, q, k, v, do, 1, scale, f"causal gqa D{D}", causal=True)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_grouped_matches_repeated_heads(D):
+    """Each query head reads its group's key/value head, so O, LSE and dQ
+    equal (bit for bit) the plain entry points on key/value heads repeated
+    to H; with H_kv = H the grouped entry points are the plain ones."""
+    B, n, H, Hkv, b = 2, 200, 6, 2, 8
+    q, k, v, do = make_inputs(B, n, H, D, seed=9500 + D, H_kv=Hkv)
+    scale = 1 / math.sqrt(D)
+    g = run_grouped(q, k, v, do, b, scale)
+    rk, rv = (x.repeat_interleave(H // Hkv, dim=2).contiguous() for x in (k, v))
+    m = run_diffusion(q, rk, rv, do, b, scale)
+    for key in ("out", "lse", "dq"):
+        assert torch.equal(g[key], m[key]), key
+    same = run_grouped(q, rk, rv, do, b, scale)
+    for key in m:
+        assert torch.equal(same[key], m[key]), key
+
+
+@pytest.mark.parametrize("name", sorted(n for n in GQA_WORKLOADS if n != "g2"))
+def test_grouped_workload_heads(name):
+    w = GQA_WORKLOADS[name]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_grouped(q, k, v, do, w.b, scale)
+    # first and last key/value head; a multi-query problem has one group of
+    # all H query heads per sample, checked on the last sample
+    groups = [(0, 0), (w.B - 1, w.kv_heads - 1)] if w.kv_heads > 1 else [(w.B - 1, 0)]
+    compare_grouped(res, q, k, v, do, w.b, scale, name, groups=groups)
+
+
+def test_grouped_long_workload_sampled():
+    """The long-sequence grouped problem: for one key/value head, all rows of
+    O and LSE of its query heads, sampled dQ rows of each, and dK / dV on
+    sampled key columns (summed over the group by the oracle)."""
+    w = GQA_WORKLOADS["g2"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    res = run_grouped(q, k, v, do, w.b, scale)
+    rng = np.random.default_rng(5)
+    n, G = w.n, w.H // w.kv_heads
+    bi, j = 1, w.kv_heads - 1
+    f = lambda x: oracle.to_f64(x)
+    kh, vh = f(k[bi, :, j]), f(v[bi, :, j])
+    pos = _sample_positions(n, w.b, rng, 16)
+    rows = np.array(pos + [n + p for p in pos])
+    qs, dos, outs, lses = [], [], [], []
+    for h in range(j * G, (j + 1) * G):
+        qh, dh = f(q[bi, :, h]), f(do[bi, :, h])
+        O = np.empty((2 * n, w.D))
+        L = np.empty(2 * n)
+        for r0 in range(0, 2 * n, 2048):
+            rr = np.arange(r0, r0 + 2048)
+            O[rr], L[rr] = oracle.diffusion_forward_rows(qh, kh, vh, w.b, scale, rr)
+        tag = f"g2 sample {bi} head {h}"
+        check_fwd(res["out"][bi, :, h], res["lse"][bi, h], O, L, tag)
+        dq_ref = oracle.diffusion_grad_q_rows(qh, kh, vh, dh, w.b, scale, rows)
+        check_grad(res["dq"][bi, rows, h], dq_ref, "dq", tag)
+        qs.append(qh)
+        dos.append(dh)
+        outs.append(O)
+        lses.append(L)
+    dk_ref, dv_ref = oracle.grouped_grad_kv_cols(qs, kh, vh, dos, outs, lses, w.b, scale, rows)
+    check_grad(res["dk"][bi, rows, j], dk_ref, "dk", f"g2 kv head {j}")
+    check_grad(res["dv"][bi, rows, j], dv_ref, "dv", f"g2 kv head {j}")
+
+
+def test_grouped_autograd_wrapper():
+    dev = _dev()
+    q, k, v, do = make_inputs(2, 96, 4, 64, seed=9600, H_kv=2)
+    ref = run_grouped(q, k, v, do, 4, 0.125)
+    tq, tk, tv = (x.to(dev).requires_grad_() for x in (q, k, v))
+    out, lse = bd.diffusion_attn_func(tq, tk, tv, 4, softmax_scale=0.125, return_lse=True)
+    out.backward(do.to(dev))
+    assert torch.equal(out.detach().cpu(), ref["out"])
+    assert torch.equal(lse.cpu(), ref["lse"])
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert torch.equal(t.grad.cpu(), ref[name]), name
