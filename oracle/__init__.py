@@ -27,6 +27,8 @@ from .attention import (  # noqa: F401
     grouped_forward,
     grouped_backward,
     grouped_grad_kv_cols,
+    varlen_forward,
+    varlen_backward,
     batched,
     to_f64,
 )

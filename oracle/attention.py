@@ -273,6 +273,63 @@ def grouped_grad_kv_cols(qs, k, v, douts, outs, lses, b: int, scale: float, cols
 
 
 # --------------------------------------------------------------------------
+# Variable-length batches: samples of different lengths packed in one tensor
+# --------------------------------------------------------------------------
+#
+# Fast Diffusion Attention, "Hopper" (varlen batches: packed samples of
+# different lengths) and "Try it" (the varlen function follows
+# flash-attention's varlen call).  Reading taken: sample b occupies the
+# packed tokens [cu[b], cu[b+1]); in the diffusion layout those are its
+# noisy half followed by its clean half (2 n_b tokens), in the causal
+# layout one sequence.  A sample attends only within itself, exactly as
+# the batched function on that sample alone.  Per-row statistics are laid
+# out [heads][total tokens].
+
+def varlen_forward(fn: Callable, q, k, v, cu: Sequence[int], **kw):
+    """(O, LSE) of packed q (total, H, D) against k, v (total, H_kv, D).
+
+    ``fn`` is a one-head forward (``diffusion_forward`` or
+    ``causal_forward``-like, taking q, k, v of one sample and head).
+    Tokens outside every sample are NaN.
+    """
+    total, H, D = q.shape
+    H_kv = k.shape[1]
+    O = np.full((total, H, D), np.nan)
+    L = np.full((H, total), np.nan)
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue                      # an empty sample has no rows
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            O[s0:s1, h], L[h, s0:s1] = fn(q[s0:s1, h], k[s0:s1, j], v[s0:s1, j], **kw)
+    return O, L
+
+
+def varlen_backward(fn: Callable, q, k, v, dout, cu: Sequence[int], **kw):
+    """(dq, dk, dv) of packed tensors; dk and dv of a key/value head sum over
+    its query heads.  Tokens outside every sample are NaN."""
+    total, H, D = q.shape
+    H_kv = k.shape[1]
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        dk[s0:s1] = 0.0
+        dv[s0:s1] = 0.0
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            gq, gk, gv = fn(q[s0:s1, h], k[s0:s1, j], v[s0:s1, j], dout[s0:s1, h], **kw)
+            dq[s0:s1, h] = gq
+            dk[s0:s1, j] += gk
+            dv[s0:s1, j] += gv
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
 # (batch, seq, heads, dim) helpers
 # --------------------------------------------------------------------------
 

@@ -17,7 +17,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from workloads import WORKLOADS, make_inputs
+from workloads import WORKLOADS, cu_seqlens, make_inputs, make_varlen_inputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -440,3 +440,79 @@ def test_grouped_inputs_keep_the_mha_draws():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     q, k, v, do = make_inputs(1, 8, 4, 4, seed=3, H_kv=2)
     assert q.shape == do.shape == (1, 16, 4, 4) and k.shape == v.shape == (1, 16, 2, 4)
+
+
+# --------------------------------------------------------------------------
+# Variable-length (packed) batches
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,H_kv", [(3, 3), (4, 2)])
+def test_varlen_with_equal_lengths_is_the_batched_oracle(H, H_kv):
+    """Packing B samples of one length back to back is the (B, 2n, H, D)
+    layout flattened: the packed oracle must reproduce the batched one."""
+    B, n, D, b, scale = 3, 9, 4, 2, 0.6
+    q, k, v, do = (oracle.to_f64(x) for x in make_inputs(B, n, H, D, seed=70 + H_kv, H_kv=H_kv))
+    cu = cu_seqlens([n] * B)
+    flat = lambda x: x.reshape(B * 2 * n, *x.shape[2:])
+    O, L = oracle.varlen_forward(oracle.diffusion_forward, flat(q), flat(k), flat(v), cu, b=b, scale=scale)
+    g = oracle.varlen_backward(oracle.diffusion_backward, flat(q), flat(k), flat(v), flat(do), cu,
+                               b=b, scale=scale)
+    Ob, Lb = oracle.grouped_forward(oracle.diffusion_forward, q, k, v, b=b, scale=scale)
+    gb = oracle.grouped_backward(oracle.diffusion_backward, q, k, v, do, b=b, scale=scale)
+    np.testing.assert_allclose(O, flat(Ob), atol=1e-13)
+    np.testing.assert_allclose(L, Lb.transpose(1, 0, 2).reshape(H, B * 2 * n), atol=1e-13)
+    for x, y in zip(g, gb):
+        np.testing.assert_allclose(x, flat(y), atol=1e-12)
+
+
+def test_varlen_each_sample_uses_its_own_length():
+    """q = 0 with samples of lengths 5, 0, 1, 8, 3: every row averages the
+    visible values of its own sample, LSE = ln(count) from that sample's
+    own mask (an empty sample has no rows)."""
+    ns, b, D = [5, 0, 1, 8, 3], 2, 3
+    cu = cu_seqlens(ns)
+    total = cu[-1]
+    v = _rand((total, 2, D), 71)
+    k = _rand((total, 2, D), 72)
+    O, L = oracle.varlen_forward(oracle.diffusion_forward, np.zeros((total, 2, D)), k, v, cu, b=b, scale=1.0)
+    for bi, nb in enumerate(ns):
+        if nb == 0:
+            continue
+        M = _prose_mask(nb, b)
+        s0 = cu[bi]
+        for r in range(2 * nb):
+            for h in range(2):
+                np.testing.assert_allclose(O[s0 + r, h], v[s0:s0 + 2 * nb, h][M[r]].mean(axis=0), atol=1e-12)
+                assert abs(L[h, s0 + r] - math.log(M[r].sum())) < 1e-12
+    assert not np.isnan(O).any()
+
+
+def test_varlen_samples_do_not_interact():
+    """Changing one sample's keys and values leaves every other sample's
+    outputs and gradients unchanged."""
+    ns, b, D, scale = [4, 6, 0, 3], 3, 4, 0.8
+    cu = cu_seqlens(ns)
+    total = cu[-1]
+    q, k, v, do = (_rand((total, 2, D), s) for s in (73, 74, 75, 76))
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[1]:cu[2]] += 1.5
+    v2[cu[1]:cu[2]] -= 2.0
+    O, _ = oracle.varlen_forward(oracle.diffusion_forward, q, k, v, cu, b=b, scale=scale)
+    O2, _ = oracle.varlen_forward(oracle.diffusion_forward, q, k2, v2, cu, b=b, scale=scale)
+    g = oracle.varlen_backward(oracle.diffusion_backward, q, k, v, do, cu, b=b, scale=scale)
+    g2 = oracle.varlen_backward(oracle.diffusion_backward, q, k2, v2, do, cu, b=b, scale=scale)
+    other = np.r_[cu[0]:cu[1], cu[3]:cu[4]]
+    np.testing.assert_array_equal(O[other], O2[other])
+    for x, y in zip(g, g2):
+        np.testing.assert_array_equal(x[other], y[other])
+    assert not np.allclose(O[cu[1]:cu[2]], O2[cu[1]:cu[2]])
+
+
+def test_varlen_inputs_are_seeded_and_packed():
+    ns = [3, 0, 5]
+    q, k, v, do, cu = make_varlen_inputs(ns, 4, 8, seed=9, H_kv=2)
+    assert cu == [0, 6, 6, 16]
+    assert q.shape == do.shape == (16, 4, 8) and k.shape == v.shape == (16, 2, 8)
+    q2, *_ = make_varlen_inputs(ns, 4, 8, seed=9, H_kv=2)
+    assert torch.equal(q, q2)
+    assert cu_seqlens(ns, causal=True) == [0, 3, 3, 8]

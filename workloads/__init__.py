@@ -18,7 +18,7 @@ workloads below stand in for them.
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Tuple
+from typing import Dict, List, Sequence, Tuple
 
 import torch
 
@@ -81,6 +81,52 @@ GQA_WORKLOADS: Dict[str, Workload] = {
     "g3": Workload("g3", B=4, n=2048, H=16, D=64, b=4, seed=1013, H_kv=1),
 }
 
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """B packed samples whose half lengths n_b are drawn uniformly from
+    [n_min, n_max] (CPU torch.Generator seeded with len_seed, drawn before
+    and apart from the tensors); H query heads, H_kv key/value heads
+    (0: H), width D, block size b; tensors from ``seed``."""
+
+    name: str
+    B: int
+    n_min: int
+    n_max: int
+    H: int
+    D: int
+    b: int
+    seed: int
+    len_seed: int
+    H_kv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
+
+    @property
+    def half_lengths(self) -> List[int]:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(int(self.len_seed))
+        return torch.randint(self.n_min, self.n_max + 1, (self.B,), generator=g).tolist()
+
+    def describe(self) -> str:
+        kv = f" H_kv={self.kv_heads}" if self.kv_heads != self.H else ""
+        ns = self.half_lengths
+        return (f"{self.name}: varlen B={self.B} n_b in [{self.n_min}, {self.n_max}] "
+                f"(total {2 * sum(ns)} tokens, max n {max(ns)}) H={self.H}{kv} D={self.D} "
+                f"b={self.b} seed={self.seed}")
+
+
+# Packed batches of samples of random lengths (the pages' SFT-style varlen
+# workload): multi-head D=128, and grouped heads at D=64 with short samples.
+VARLEN_WORKLOADS: Dict[str, VarlenWorkload] = {
+    "v1": VarlenWorkload("v1", B=16, n_min=256, n_max=4096, H=16, D=128, b=32, seed=1021, len_seed=1022),
+    "v2": VarlenWorkload("v2", B=24, n_min=64, n_max=2048, H=32, D=64, b=4, seed=1023, len_seed=1024,
+                         H_kv=8),
+}
+
 LARGEST = "c4"
 
 
@@ -118,3 +164,33 @@ def make_causal_view(x: torch.Tensor) -> torch.Tensor:
     """
     B, twon, H, D = x.shape
     return x.reshape(2 * B, twon // 2, H, D)
+
+
+def cu_seqlens(half_lengths: Sequence[int], causal: bool = False) -> List[int]:
+    """Cumulative token offsets of packed samples: sample b occupies tokens
+    [cu[b], cu[b+1]), 2 n_b of them ([noisy | clean]), or n_b in the causal
+    layout."""
+    cu = [0]
+    for nb in half_lengths:
+        cu.append(cu[-1] + (nb if causal else 2 * nb))
+    return cu
+
+
+def make_varlen_inputs(half_lengths: Sequence[int], H: int, D: int, seed: int, H_kv: int = 0,
+                       causal: bool = False):
+    """Packed bf16 CPU tensors (q, k, v, dout) of shape (total, heads, D) --
+    q and dout with H heads, k and v with H_kv (0: H) -- and the offsets
+    ``cu``.  Same draw order and rounding as ``make_inputs``."""
+    cu = cu_seqlens(half_lengths, causal)
+    total = cu[-1]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    kv = H_kv or H
+    out = []
+    for heads in (H, kv, kv, H):
+        out.append(torch.randn((total, heads, D), generator=g, dtype=torch.float32).to(torch.bfloat16))
+    return (*out, cu)
+
+
+def make_varlen_workload_inputs(w: VarlenWorkload):
+    return make_varlen_inputs(w.half_lengths, w.H, w.D, w.seed, H_kv=w.H_kv)
