@@ -20,7 +20,10 @@ Prints one JSON line.  Default workload: the long-sequence problem
 time of the same kernels run ungrouped, on key/value heads repeated to H
 (without the reduction of dK / dV over the group that this would still
 need): the saving of the grouped backward (Fast Diffusion Attention,
-"Ampere and Ada").
+"Ampere and Ada").  The packed workloads (v1, v2: samples of random
+lengths) count the visible pairs of every sample, and their yardstick is
+the causal kernel on the same packed bytes, each half of each sample one
+sequence.
 """
 from __future__ import annotations
 
@@ -62,9 +65,11 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, q, k, v, do, target_s=10.0, chunk=2048):
+def cpu_baseline(heads, name, target_s=10.0, chunk=2048):
     """Time the float64 oracle (as it stands) on a bounded sample of the same
-    workload: whole (sample, head) pairs, processed in chunks of query rows
+    workload: whole (sample, head) problems, taken in the order ``heads``
+    yields them (q, k, v, dout of one head as bf16 CPU tensors, the half
+    length n and the block size b), each processed in chunks of query rows
     (forward and backward of each chunk against all 2n keys), until about
     target_s seconds of CPU work have been done."""
     import numpy as np
@@ -74,46 +79,38 @@ def cpu_baseline(w, q, k, v, do, target_s=10.0, chunk=2048):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = 1
-    n, scale = w.n, 1.0 / math.sqrt(w.D)
-    G = w.H // w.kv_heads
-    pairs, chunks, heads = 0, 0, 0
+    pairs, chunks, done_heads, D = 0, 0, 0, None
     t_fwd = t_bwd = 0.0
     t_start = time.perf_counter()
-    done = False
-    for bi in range(w.B):
-        for hi in range(w.H):
-            qh, dh = oracle.to_f64(q[bi, :, hi]), oracle.to_f64(do[bi, :, hi])
-            kh, vh = oracle.to_f64(k[bi, :, hi // G]), oracle.to_f64(v[bi, :, hi // G])
-            for r0 in range(0, 2 * n, chunk):
-                rows = np.arange(r0, min(r0 + chunk, 2 * n))
-                M = oracle.block_diffusion_mask(n, w.b, rows)
-                pairs += int(M.sum())
-                t0 = time.perf_counter()
-                oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
-                t1 = time.perf_counter()
-                oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
-                t2 = time.perf_counter()
-                t_fwd += t1 - t0
-                t_bwd += t2 - t1
-                chunks += 1
-                if time.perf_counter() - t_start >= target_s and r0 + chunk >= 2 * n:
-                    done = True
-                    break
-            heads += 1
-            if done:
-                break
-        if done:
+    for qh, kh, vh, dh, n, b in heads:
+        qh, kh, vh, dh = (oracle.to_f64(x) for x in (qh, kh, vh, dh))
+        D = qh.shape[1]
+        scale = 1.0 / math.sqrt(D)
+        for r0 in range(0, 2 * n, chunk):
+            rows = np.arange(r0, min(r0 + chunk, 2 * n))
+            M = oracle.block_diffusion_mask(n, b, rows)
+            pairs += int(M.sum())
+            t0 = time.perf_counter()
+            oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
+            t1 = time.perf_counter()
+            oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
+            chunks += 1
+        done_heads += 1
+        if time.perf_counter() - t_start >= target_s:
             break
-    flops = 3.5 * 4 * pairs * w.D
+    flops = 3.5 * 4 * pairs * D
     return {
         "value": flops / (t_fwd + t_bwd) / 1e12,
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"float64 oracle forward + backward of {heads} whole (sample, head) pair(s) of {w.name} "
-                   f"({chunks} chunks of {chunk} query rows against all {2 * n} keys; {pairs} visible pairs); "
-                   f"{t_fwd:.1f} s forward + {t_bwd:.1f} s backward; BLAS threads {cores}; "
-                   f"host {platform.processor() or platform.machine()}"),
+        "sample": (f"float64 oracle forward + backward of {done_heads} whole (sample, head) pair(s) of {name} "
+                   f"({chunks} chunks of up to {chunk} query rows against all keys of their sample; "
+                   f"{pairs} visible pairs); {t_fwd:.1f} s forward + {t_bwd:.1f} s backward; "
+                   f"BLAS threads {cores}; host {platform.processor() or platform.machine()}"),
     }
 
 
@@ -173,6 +170,175 @@ class ClockSampler:
                 "max_mhz": max(self.samples), "samples": len(self.samples), "source": "amdsmi SYS clock"}
 
 
+class Problem:
+    """The timed work of one workload: a diffusion step and the causal
+    yardstick step on the same bytes, with their visible-pair counts."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def new_events(torch):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+
+def mark(ev, i):
+    """Record event i of a step: 0 before the forward, 1 after it, 2 after dQ, 3 after dK/dV."""
+    if ev is not None:
+        ev[i].record()
+
+
+def setup_batched(w, dev, torch, bd):
+    """(B, 2n, H, D) tensors; the yardstick views them as (2B, n, H, D)."""
+    from workloads import make_workload_inputs
+    B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
+    scale = 1.0 / math.sqrt(D)
+    cpu = make_workload_inputs(w)
+    q, k, v, do = (x.to(dev) for x in cpu)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, 2 * n), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cq, cdo = (x.view(2 * B, n, H, D) for x in (q, do))
+    ck, cv = (x.view(2 * B, n, Hkv, D) for x in (k, v))
+    cout = torch.empty_like(cq)
+    clse = torch.empty((2 * B, H, n), dtype=torch.float32, device=dev)
+    cdq = torch.empty_like(cq)
+    cdk, cdv = torch.empty_like(ck), torch.empty_like(cv)
+    cws = torch.empty(bd.causal_attn_bwd_gqa_workspace_size(2 * B, n, H, Hkv, D), dtype=torch.uint8,
+                      device=dev)
+    MD, MC = bd.MODE_DIFFUSION, bd.MODE_CAUSAL
+
+    def diffusion_step(ev=None):
+        mark(ev, 0)
+        if Hkv == H:
+            bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+        else:
+            bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
+        mark(ev, 1)
+        for stage in range(2):
+            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, Hkv, D, b,
+                                scale, ws, ws_bytes)
+            mark(ev, 2 + stage)
+
+    def causal_step(ev=None):
+        mark(ev, 0)
+        if Hkv == H:
+            bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
+        else:
+            bd.causal_attn_fwd_gqa(cq, ck, cv, cout, clse, 2 * B, n, H, Hkv, D, scale)
+        mark(ev, 1)
+        for stage in range(2):
+            bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, None, 2 * B, n, 0,
+                                H, Hkv, D, 1, scale, cws)
+            mark(ev, 2 + stage)
+
+    def ungrouped():
+        """Backward of the same kernels on key/value heads repeated to H."""
+        if Hkv == H:
+            return None
+        G = H // Hkv
+        ek, ev_ = (x.repeat_interleave(G, dim=2).contiguous() for x in (k, v))
+        edk, edv = torch.empty_like(q), torch.empty_like(q)
+        times = {"grouped": [], "ungrouped": []}
+        for _ in range(3):
+            for name, kk, vv, gk, gv, hk in (("grouped", k, v, dk, dv, Hkv), ("ungrouped", ek, ev_, edk, edv, H)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 5
+                e0.record()
+                for _ in range(reps):
+                    for stage in range(2):
+                        bd.bdattn_bwd_stage(MD, stage, q, kk, vv, out, do, lse, dq, gk, gv, None, B, n, 0, H,
+                                            hk, D, b, scale, ws, ws_bytes)
+                e1.record()
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1) / reps)
+        med = {name: statistics.median(x) for name, x in times.items()}
+        return {"bwd_ms_grouped": med["grouped"], "bwd_ms_ungrouped": med["ungrouped"],
+                "speedup": med["ungrouped"] / med["grouped"],
+                "note": "ungrouped = the same kernels on key/value heads repeated to H, "
+                        "without the dK/dV reduction over the group"}
+
+    def cpu_heads():
+        G = H // Hkv
+        for bi in range(B):
+            for hi in range(H):
+                yield cpu[0][bi, :, hi], cpu[1][bi, :, hi // G], cpu[2][bi, :, hi // G], cpu[3][bi, :, hi], n, b
+
+    P = visible_pairs(n, b)
+    assert P == bd.bdattn_visible_pairs(MD, n, b)
+    return Problem(diffusion_step=diffusion_step, causal_step=causal_step, ungrouped=ungrouped,
+                   cpu_heads=cpu_heads, pair_heads=P * H * B, causal_pair_heads=n * (n + 1) // 2 * H * 2 * B,
+                   config={"workload": w.describe(), "global_batch": B, "seq_len": 2 * n, "block_size": b,
+                           "heads": H, "kv_heads": Hkv, "headdim": D, "parallelism": "single-gpu"})
+
+
+def setup_varlen(w, dev, torch, bd):
+    """Packed samples of random lengths; the yardstick packs the same bytes
+    as 2B causal sequences (each half of each sample)."""
+    from workloads import cu_seqlens, make_varlen_workload_inputs
+    ns = w.half_lengths
+    B, H, Hkv, D, b = w.B, w.H, w.kv_heads, w.D, w.b
+    max_n = max(ns)
+    scale = 1.0 / math.sqrt(D)
+    cpu = make_varlen_workload_inputs(w)
+    q, k, v, do = (x.to(dev) for x in cpu[:4])
+    cu = cpu[4]
+    total = cu[-1]
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+    ccu_t = torch.tensor(cu_seqlens([x for nb in ns for x in (nb, nb)], causal=True), dtype=torch.int32,
+                         device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bd.diffusion_attn_varlen_bwd_workspace_size(B, max_n, total, H, Hkv, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cout = torch.empty_like(q)
+    clse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    cdq = torch.empty_like(q)
+    cdk, cdv = torch.empty_like(k), torch.empty_like(v)
+    cws_bytes = bd.causal_attn_varlen_bwd_workspace_size(2 * B, max_n, total, H, Hkv, D)
+    cws = torch.empty(cws_bytes, dtype=torch.uint8, device=dev)
+    MD, MC = bd.MODE_DIFFUSION, bd.MODE_CAUSAL
+
+    def diffusion_step(ev=None):
+        mark(ev, 0)
+        bd.diffusion_attn_varlen_fwd(q, k, v, out, lse, cu_t, B, max_n, total, H, Hkv, D, b, scale)
+        mark(ev, 1)
+        for stage in range(2):
+            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, cu_t, B, max_n, total, H, Hkv,
+                                D, b, scale, ws, ws_bytes)
+            mark(ev, 2 + stage)
+
+    def causal_step(ev=None):
+        mark(ev, 0)
+        bd.causal_attn_varlen_fwd(q, k, v, cout, clse, ccu_t, 2 * B, max_n, total, H, Hkv, D, scale)
+        mark(ev, 1)
+        for stage in range(2):
+            bd.bdattn_bwd_stage(MC, stage, q, k, v, cout, do, clse, cdq, cdk, cdv, ccu_t, 2 * B, max_n, total,
+                                H, Hkv, D, 1, scale, cws, cws_bytes)
+            mark(ev, 2 + stage)
+
+    def cpu_heads():
+        G = H // Hkv
+        for bi in sorted(range(B), key=lambda i: -ns[i]):
+            s0, s1 = cu[bi], cu[bi + 1]
+            for hi in range(H):
+                yield (cpu[0][s0:s1, hi], cpu[1][s0:s1, hi // G], cpu[2][s0:s1, hi // G], cpu[3][s0:s1, hi],
+                       ns[bi], b)
+
+    P = sum(visible_pairs(nb, b) for nb in ns if nb > 0)
+    return Problem(diffusion_step=diffusion_step, causal_step=causal_step, ungrouped=lambda: None,
+                   cpu_heads=cpu_heads, pair_heads=P * H,
+                   causal_pair_heads=sum(nb * (nb + 1) for nb in ns) * H,
+                   config={"workload": w.describe(), "global_batch": B, "seq_len": 2 * max_n,
+                           "total_tokens": total, "block_size": b, "heads": H, "kv_heads": Hkv,
+                           "headdim": D, "parallelism": "single-gpu"})
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,90 +350,33 @@ def main():
 
     import torch
     import block_diffusion_lm_amd as bd
-    from workloads import GQA_WORKLOADS, WORKLOADS, make_workload_inputs
+    from workloads import GQA_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS
 
-    all_workloads = {**WORKLOADS, **GQA_WORKLOADS}
-    if args.workload not in all_workloads:
-        print(f"unknown workload {args.workload!r}; known: {', '.join(all_workloads)}", file=sys.stderr)
+    batched = {**WORKLOADS, **GQA_WORKLOADS}
+    if args.workload in batched:
+        w, setup = batched[args.workload], setup_batched
+    elif args.workload in VARLEN_WORKLOADS:
+        w, setup = VARLEN_WORKLOADS[args.workload], setup_varlen
+    else:
+        known = ", ".join(list(batched) + list(VARLEN_WORKLOADS))
+        print(f"unknown workload {args.workload!r}; known: {known}", file=sys.stderr)
         sys.exit(2)
-    w = all_workloads[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
-    T = 2 * n
-    scale = 1.0 / math.sqrt(D)
-
-    q_c, k_c, v_c, do_c = make_workload_inputs(w)
-    q, k, v, do = (x.to(dev) for x in (q_c, k_c, v_c, do_c))
-    out = torch.empty_like(q)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    dq = torch.empty_like(q)
-    dk, dv = torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, Hkv, D)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-
-    # causal yardstick: the same bytes as 2B sequences of n tokens
-    cq, cdo = (x.view(2 * B, n, H, D) for x in (q, do))
-    ck, cv = (x.view(2 * B, n, Hkv, D) for x in (k, v))
-    cout = torch.empty_like(cq)
-    clse = torch.empty((2 * B, H, n), dtype=torch.float32, device=dev)
-    cdq = torch.empty_like(cq)
-    cdk, cdv = torch.empty_like(ck), torch.empty_like(cv)
-    cws = torch.empty(bd.causal_attn_bwd_gqa_workspace_size(2 * B, n, H, Hkv, D), dtype=torch.uint8,
-                      device=dev)
-
-    MD, MC = bd.MODE_DIFFUSION, bd.MODE_CAUSAL
-
-    def fwd_diffusion():
-        if Hkv == H:
-            bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
-        else:
-            bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
-
-    def fwd_causal():
-        if Hkv == H:
-            bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
-        else:
-            bd.causal_attn_fwd_gqa(cq, ck, cv, cout, clse, 2 * B, n, H, Hkv, D, scale)
-
-    def diffusion_step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        fwd_diffusion()
-        if ev is not None:
-            ev[1].record()
-        for stage in range(2):
-            bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, B, n, H, Hkv, D, b, scale,
-                                ws, ws_bytes)
-            if ev is not None:
-                ev[2 + stage].record()
-
-    def causal_step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        fwd_causal()
-        if ev is not None:
-            ev[1].record()
-        for stage in range(2):
-            bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, 2 * B, n, H, Hkv,
-                                D, 1, scale, cws)
-            if ev is not None:
-                ev[2 + stage].record()
-
-    def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    prob = setup(w, dev, torch, bd)
+    D = w.D
 
     # ---- warm-up, then exactly K timed steps --------------------------------
     for _ in range(args.warmup):
-        diffusion_step()
+        prob.diffusion_step()
     torch.cuda.synchronize()
-    evs = [new_events() for _ in range(args.steps)]
+    evs = [new_events(torch) for _ in range(args.steps)]
     clock = ClockSampler()
     torch.cuda.synchronize()
     clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        diffusion_step(evs[i])
+        prob.diffusion_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clock.stop()
@@ -284,18 +393,17 @@ def main():
     kern = split(evs)
     kern_avg = {key: sum(vals) / len(vals) for key, vals in kern.items()}
 
-    P = visible_pairs(n, b)
-    assert P == bd.bdattn_visible_pairs(MD, n, b)
-    F_fwd = 4.0 * P * D * H * B
+    PH = prob.pair_heads          # visible (query, key) pairs summed over samples and heads
+    F_fwd = 4.0 * PH * D
     F_bwd = 2.5 * F_fwd
     value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
     t_fwd = kern_avg["fwd"]
     t_bwd = kern_avg["bwd_dq"] + kern_avg["bwd_dkdv"]
 
     # ---- the dominant kernel against its roofline ---------------------------
-    per_kernel_flops = {"fwd": 2 * 2.0 * P * D * H * B,        # S = QK^T, O = PV
-                        "bwd_dkdv": 4 * 2.0 * P * D * H * B,   # S, dP, dV, dK
-                        "bwd_dq": 3 * 2.0 * P * D * H * B}     # S, dP, dQ
+    per_kernel_flops = {"fwd": 2 * 2.0 * PH * D,        # S = QK^T, O = PV
+                        "bwd_dkdv": 4 * 2.0 * PH * D,   # S, dP, dV, dK
+                        "bwd_dq": 3 * 2.0 * PH * D}     # S, dP, dQ
     dom = max(per_kernel_flops, key=lambda kname: kern_avg[kname])
     achieved = per_kernel_flops[dom] / (kern_avg[dom] * 1e-3) / 1e12
     # HBM bytes per launch from the rocprofv3 counter runs, valid only while
@@ -315,14 +423,14 @@ def main():
     medians = None
     if not args.no_causal:
         for _ in range(2):
-            causal_step()
+            prob.causal_step()
         torch.cuda.synchronize()
         reps = max(1, int(math.ceil(args.round_ms / max(ms_per_step, 1e-3))))
         rounds = {"diff": [], "causal": []}
         clock.start()
         for _ in range(args.rounds):
-            for name, fn in (("diff", diffusion_step), ("causal", causal_step)):
-                ev_list = [new_events() for _ in range(reps)]
+            for name, fn in (("diff", prob.diffusion_step), ("causal", prob.causal_step)):
+                ev_list = [new_events(torch) for _ in range(reps)]
                 for i in range(reps):
                     fn(ev_list[i])
                 torch.cuda.synchronize()
@@ -333,8 +441,7 @@ def main():
         clock.stop()
         med = {name: (statistics.median(x[0] for x in r), statistics.median(x[1] for x in r),
                       statistics.median(x[0] + x[1] for x in r)) for name, r in rounds.items()}
-        Pc = n * (n + 1) // 2
-        Fc_fwd = 4.0 * Pc * D * H * (2 * B)
+        Fc_fwd = 4.0 * prob.causal_pair_heads * D
         tf = lambda F, ms: F / (ms * 1e-3) / 1e12
         medians = {
             "diffusion_tflops": {"fwd": tf(F_fwd, med["diff"][0]), "bwd": tf(F_bwd, med["diff"][1]),
@@ -346,31 +453,7 @@ def main():
         ratio = {kname: medians["diffusion_tflops"][kname] / medians["causal_tflops"][kname]
                  for kname in ("fwd", "bwd", "step")}
 
-    # ---- grouped-query workloads: the backward run ungrouped ----------------
-    ungrouped = None
-    if Hkv != H:
-        G = H // Hkv
-        ek, ev_ = (x.repeat_interleave(G, dim=2).contiguous() for x in (k, v))
-        edk, edv = torch.empty_like(q), torch.empty_like(q)
-        times = {"grouped": [], "ungrouped": []}
-        for _ in range(3):
-            for name, kk, vv, gk, gv, hk in (("grouped", k, v, dk, dv, Hkv), ("ungrouped", ek, ev_, edk, edv, H)):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 5
-                e0.record()
-                for _ in range(reps):
-                    for stage in range(2):
-                        bd.bdattn_bwd_stage(MD, stage, q, kk, vv, out, do, lse, dq, gk, gv, B, n, H, hk, D, b,
-                                            scale, ws, ws_bytes)
-                e1.record()
-                torch.cuda.synchronize()
-                times[name].append(e0.elapsed_time(e1) / reps)
-        med = {name: statistics.median(x) for name, x in times.items()}
-        ungrouped = {"bwd_ms_grouped": med["grouped"], "bwd_ms_ungrouped": med["ungrouped"],
-                     "speedup": med["ungrouped"] / med["grouped"],
-                     "note": "ungrouped = the same kernels on key/value heads repeated to H, "
-                             "without the dK/dV reduction over the group"}
-        del ek, ev_, edk, edv
+    ungrouped = prob.ungrouped()
 
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -380,7 +463,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
+        cpu = cpu_baseline(prob.cpu_heads(), w.name, args.cpu_seconds)
 
     line = {
         "metric": "fwd+bwd TFLOPS (visible pairs only) and ratio vs own causal kernel on 2B×n",
@@ -395,8 +478,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.describe(), "global_batch": B, "seq_len": T, "block_size": b,
-                   "heads": H, "kv_heads": Hkv, "headdim": D, "parallelism": "single-gpu"},
+        "config": prob.config,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fwd_tflops": F_fwd / (t_fwd * 1e-3) / 1e12,

@@ -22,13 +22,23 @@ from ._binding import (  # noqa: F401
     causal_attn_bwd_workspace_size,
     causal_attn_fwd,
     causal_attn_fwd_gqa,
+    causal_attn_varlen_bwd,
+    causal_attn_varlen_bwd_workspace_size,
+    causal_attn_varlen_fwd,
     diffusion_attn_bwd,
     diffusion_attn_bwd_gqa,
     diffusion_attn_bwd_gqa_workspace_size,
     diffusion_attn_bwd_workspace_size,
     diffusion_attn_fwd,
     diffusion_attn_fwd_gqa,
+    diffusion_attn_varlen_bwd,
+    diffusion_attn_varlen_bwd_workspace_size,
+    diffusion_attn_varlen_fwd,
     lib,
     status_string,
 )
-from .autograd import causal_attn_func, diffusion_attn_func  # noqa: F401
+from .autograd import (  # noqa: F401
+    causal_attn_func,
+    diffusion_attn_func,
+    diffusion_attn_varlen_func,
+)

@@ -31,7 +31,13 @@ SIGNATURES = {
     "causal_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
-    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 9 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 10 + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "diffusion_attn_varlen_fwd": (_i, [_vp] * 6 + [_i] * 7 + [_f, _vp]),
+    "diffusion_attn_varlen_bwd_workspace_size": (_sz, [_i] * 6),
+    "diffusion_attn_varlen_bwd": (_i, [_vp] * 10 + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "causal_attn_varlen_fwd": (_i, [_vp] * 6 + [_i] * 6 + [_f, _vp]),
+    "causal_attn_varlen_bwd_workspace_size": (_sz, [_i] * 6),
+    "causal_attn_varlen_bwd": (_i, [_vp] * 10 + [_i] * 6 + [_f, _vp, _sz, _vp]),
     "diffusion_attn_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp]),
     "diffusion_attn_bwd_gqa": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "causal_attn_fwd_gqa": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
@@ -174,16 +180,104 @@ def _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace, 
     return int(workspace_bytes)
 
 
-def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
-                     block_size, scale, workspace, workspace_bytes=None, stream=None):
-    """One backward kernel (0: dQ, also writing -delta and lse2; 1: dK/dV); n is S in causal mode."""
-    T = 2 * n if mode == MODE_DIFFUSION else n
-    wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace, workspace_bytes)
+def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, n,
+                     total_tokens, H, H_kv, D, block_size, scale, workspace, workspace_bytes=None,
+                     stream=None):
+    """One backward stage (0: dQ, also writing -delta and lse2; 1: dK/dV).
+
+    cu_seqlens None: batched tensors, n the half length (S in causal mode),
+    total_tokens ignored.  Otherwise packed tensors as in the varlen entry
+    points, n the longest sample."""
+    if cu_seqlens is None:
+        T = 2 * n if mode == MODE_DIFFUSION else n
+        wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace,
+                        workspace_bytes)
+        cu = None
+    else:
+        wsb = _want_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, total_tokens, H,
+                               H_kv, D, workspace, workspace_bytes)
+        cu = _ptr(cu_seqlens)
     _check(lib().bdattn_bwd_stage(mode, stage, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, H_kv, D,
-                                  block_size, float(scale), _ptr(workspace), wsb,
+                                  _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), cu, B, n, total_tokens,
+                                  H, H_kv, D, block_size, float(scale), _ptr(workspace), wsb,
                                   _stream_handle(q, stream)),
            "bdattn_bwd_stage")
+
+
+# Packed samples of different lengths: q / out / dout / dq [total][H][D],
+# k / v / dk / dv [total][H_kv][D], lse [H][total], cu_seqlens int32 [B + 1]
+# on the GPU (sample b: tokens cu[b] .. cu[b+1]).
+
+def _want_fwd_packed(q, k, v, out, lse, cu_seqlens, B, total, H, H_kv, D):
+    bf = torch.bfloat16
+    _want(("q", q, bf, (total, H, D)), ("k", k, bf, (total, H_kv, D)),
+          ("v", v, bf, (total, H_kv, D)), ("out", out, bf, (total, H, D)),
+          ("lse", lse, torch.float32, (H, total)), ("cu_seqlens", cu_seqlens, torch.int32, (B + 1,)))
+
+
+def _want_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, total, H, H_kv, D,
+                     workspace, workspace_bytes):
+    bf = torch.bfloat16
+    qs, kvs = (total, H, D), (total, H_kv, D)
+    _want(("q", q, bf, qs), ("k", k, bf, kvs), ("v", v, bf, kvs), ("out", out, bf, qs),
+          ("dout", dout, bf, qs), ("lse", lse, torch.float32, (H, total)), ("dq", dq, bf, qs),
+          ("dk", dk, bf, kvs), ("dv", dv, bf, kvs),
+          ("cu_seqlens", cu_seqlens, torch.int32, (B + 1,)))
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a tensor on the GPU")
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return int(workspace_bytes)
+
+
+def diffusion_attn_varlen_fwd(q, k, v, out, lse, cu_seqlens, B, max_n, total_tokens, H, H_kv, D,
+                              block_size, scale, stream=None):
+    _want_fwd_packed(q, k, v, out, lse, cu_seqlens, B, total_tokens, H, H_kv, D)
+    _check(lib().diffusion_attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           _ptr(cu_seqlens), B, max_n, total_tokens, H, H_kv, D,
+                                           block_size, float(scale), _stream_handle(q, stream)),
+           "diffusion_attn_varlen_fwd")
+
+
+def diffusion_attn_varlen_bwd_workspace_size(B, max_n, total_tokens, H, H_kv, D) -> int:
+    return int(lib().diffusion_attn_varlen_bwd_workspace_size(B, max_n, total_tokens, H, H_kv, D))
+
+
+def diffusion_attn_varlen_bwd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, max_n,
+                              total_tokens, H, H_kv, D, block_size, scale, workspace,
+                              workspace_bytes=None, stream=None):
+    wsb = _want_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, total_tokens, H, H_kv,
+                           D, workspace, workspace_bytes)
+    _check(lib().diffusion_attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens),
+                                           B, max_n, total_tokens, H, H_kv, D, block_size,
+                                           float(scale), _ptr(workspace), wsb,
+                                           _stream_handle(q, stream)),
+           "diffusion_attn_varlen_bwd")
+
+
+def causal_attn_varlen_fwd(q, k, v, out, lse, cu_seqlens, B, max_S, total_tokens, H, H_kv, D, scale,
+                           stream=None):
+    _want_fwd_packed(q, k, v, out, lse, cu_seqlens, B, total_tokens, H, H_kv, D)
+    _check(lib().causal_attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _ptr(cu_seqlens), B, max_S, total_tokens, H, H_kv, D,
+                                        float(scale), _stream_handle(q, stream)),
+           "causal_attn_varlen_fwd")
+
+
+def causal_attn_varlen_bwd_workspace_size(B, max_S, total_tokens, H, H_kv, D) -> int:
+    return int(lib().causal_attn_varlen_bwd_workspace_size(B, max_S, total_tokens, H, H_kv, D))
+
+
+def causal_attn_varlen_bwd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, max_S, total_tokens,
+                           H, H_kv, D, scale, workspace, workspace_bytes=None, stream=None):
+    wsb = _want_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, total_tokens, H, H_kv,
+                           D, workspace, workspace_bytes)
+    _check(lib().causal_attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), B, max_S,
+                                        total_tokens, H, H_kv, D, float(scale), _ptr(workspace), wsb,
+                                        _stream_handle(q, stream)),
+           "causal_attn_varlen_bwd")
 
 
 # Grouped-query attention: q / out / dout / dq carry H heads, k / v / dk / dv

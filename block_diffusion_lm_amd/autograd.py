@@ -95,6 +95,37 @@ class _CausalAttn(torch.autograd.Function):
         return dq, dk, dv, None
 
 
+class _DiffusionAttnVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_n, block_size, scale):
+        q, k, v = _prep(q), _prep(k), _prep(v)
+        total, H, D = q.shape
+        Hkv = k.shape[1]
+        B = cu_seqlens.numel() - 1
+        out = torch.empty_like(q)
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+        _b.diffusion_attn_varlen_fwd(q, k, v, out, lse, cu_seqlens, B, max_n, total, H, Hkv, D,
+                                     block_size, scale)
+        ctx.save_for_backward(q, k, v, out, lse, cu_seqlens)
+        ctx.max_n, ctx.block_size, ctx.scale = max_n, block_size, scale
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse, cu_seqlens = ctx.saved_tensors
+        dout = _prep(dout)
+        total, H, D = q.shape
+        Hkv = k.shape[1]
+        B = cu_seqlens.numel() - 1
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = _b.diffusion_attn_varlen_bwd_workspace_size(B, ctx.max_n, total, H, Hkv, D)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        _b.diffusion_attn_varlen_bwd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, ctx.max_n,
+                                     total, H, Hkv, D, ctx.block_size, ctx.scale, ws, ws_bytes)
+        return dq, dk, dv, None, None, None, None
+
+
 def diffusion_attn_func(q, k, v, block_size: int, softmax_scale=None, return_lse: bool = False):
     """Block-diffusion attention; q: (batch, 2n, heads, headdim) bf16, k and v:
     (batch, 2n, kv_heads, headdim) with heads a multiple of kv_heads."""
@@ -108,4 +139,20 @@ def causal_attn_func(q, k, v, softmax_scale=None, return_lse: bool = False):
     and v: (batch, seq, kv_heads, headdim)."""
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     out, lse = _CausalAttn.apply(q, k, v, scale)
+    return (out, lse) if return_lse else out
+
+
+def diffusion_attn_varlen_func(q, k, v, cu_seqlens, max_n: int, block_size: int, softmax_scale=None,
+                               return_lse: bool = False):
+    """Block-diffusion attention over packed samples of different lengths.
+
+    q: (total, heads, headdim) bf16, k and v: (total, kv_heads, headdim);
+    cu_seqlens: int32 (B + 1,) on the GPU, sample b holding the tokens
+    cu_seqlens[b] .. cu_seqlens[b+1] as [noisy n_b | clean n_b]; max_n: the
+    largest n_b.  Rows of the outputs and gradients outside every sample
+    are left uninitialised.  Returns out (and lse of shape (heads, total))."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    out, lse = _DiffusionAttnVarlen.apply(q, k, v, cu_seqlens, int(max_n), int(block_size), scale)
     return (out, lse) if return_lse else out

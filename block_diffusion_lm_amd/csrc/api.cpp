@@ -15,110 +15,117 @@
 
 namespace {
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, unsigned bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
-// Limits of one [B][T][H][D] tensor.  Offsets are 64-bit, but grid sizes
-// are 32-bit: the attention grids have at most ceil(T / 64) * B * H blocks.
-// B * T * H rows are capped at 2^31 - 1 (512 GB of bf16 at D = 128, more
-// than a GPU holds) so that any per-row count fits a 32-bit int.
-int check_shape(int B, int T, int H, int D) {
-  if (B < 1 || T < 1 || H < 1) return BDATTN_ERR_INVALID;
-  if (D != 64 && D != 128) return BDATTN_ERR_UNSUPPORTED;
-  const long long tiles = ((long long)T + 63) / 64 * B * H;
+// One call's problem.  Batched: B samples of T tokens (T = 2n, or n in
+// causal mode).  Packed: B samples at the token offsets cu (device memory),
+// `total` tokens in all, n the longest sample's half length (or length).
+struct Problem {
+  int mode;
+  int B, n, H, Hkv, D, b;
+  float scale;
+  const int32_t* cu;  // packed only
+  int total;          // packed only
+  bool packed() const { return cu != nullptr; }
+  int T() const { return mode == bd::MODE_CAUSAL ? n : 2 * n; }
+  long long tokens() const { return packed() ? (long long)total : (long long)B * T(); }
+};
+
+// Shape limits.  Offsets are 64-bit, grid sizes 32-bit: the attention grids
+// have at most ceil(T / 64) * B * H blocks.  All rows (tokens x H) are
+// capped at 2^31 - 1 (512 GB of bf16 at D = 128, more than a GPU holds) so
+// that any per-row count fits a 32-bit int.  The kernels address one half
+// of one sample (all heads) through a 32-bit buffer range, so T / 2 (or T)
+// tokens x H x D bf16 must stay below 2 GiB.
+int check_problem(const Problem& p) {
+  if (p.mode != bd::MODE_DIFFUSION && p.mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
+  if (p.B < 1 || p.n < 1 || p.H < 1 || p.b < 1) return BDATTN_ERR_INVALID;
+  if (p.mode == bd::MODE_DIFFUSION && p.n > std::numeric_limits<int>::max() / 2)
+    return BDATTN_ERR_INVALID;
+  if (p.D != 64 && p.D != 128) return BDATTN_ERR_UNSUPPORTED;
+  if (p.Hkv < 1 || p.Hkv > p.H || p.H % p.Hkv != 0) return BDATTN_ERR_INVALID;
+  if (p.packed() && (p.total < 1 || !aligned(p.cu, 4))) return BDATTN_ERR_INVALID;
+  const long long T = p.T();
+  const long long tiles = (T + 63) / 64 * p.B * p.H;
   if (tiles > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
-  const long long rows = (long long)B * T * H;
-  if (rows > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
-  // The kernels address one half of one sample (all heads) through a 32-bit
-  // buffer range: T/2 (or T) tokens x H x D bf16 must stay below 2 GiB.
-  if ((long long)T * H * D * 2 >= (1LL << 31)) return BDATTN_ERR_UNSUPPORTED;
+  if (p.tokens() * p.H > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
+  if (T * p.H * p.D * 2 >= (1LL << 31)) return BDATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(p.scale) || p.scale == 0.f) return BDATTN_ERR_INVALID;
   return BDATTN_OK;
 }
 
-int check_scale(float scale) {
-  return (std::isfinite(scale) && scale != 0.f) ? BDATTN_OK : BDATTN_ERR_INVALID;
+int splits_of(const Problem& p) {
+  return bd::dkdv_group_splits(p.B, p.n, p.mode == bd::MODE_CAUSAL ? 1 : 2, p.Hkv, p.H / p.Hkv);
 }
 
-// Grouped heads: 1 <= H_kv <= H and H a multiple of H_kv.
-int check_kv_heads(int H, int H_kv) {
-  return (H_kv >= 1 && H_kv <= H && H % H_kv == 0) ? BDATTN_OK : BDATTN_ERR_INVALID;
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Backward workspace: -delta and lse2 per query row ([B][H][T], or
+// [H][total] packed, float32 each), then, when the dK/dV kernel splits the
+// groups of query heads (S > 1), float32 partial dK and dV
+// ([S][tokens][Hkv][D] each).
+size_t stats_bytes(const Problem& p) {
+  return round256(2 * (size_t)p.tokens() * p.H * sizeof(float));
 }
 
-bd::AttnArgs make_args(int mode, int B, int n, int H, int H_kv, int b, float scale) {
+size_t workspace_bytes(const Problem& p) {
+  if (check_problem(p) != BDATTN_OK) return 0;
+  const int S = splits_of(p);
+  const size_t part = S > 1 ? 2 * (size_t)S * p.tokens() * p.Hkv * p.D * sizeof(float) : 0;
+  return stats_bytes(p) + round256(part);
+}
+
+bd::AttnArgs make_args(const Problem& p) {
   bd::AttnArgs a{};
-  a.B = B;
-  a.H = H;
-  a.Hkv = H_kv;
-  a.G = H / H_kv;
-  a.n = n;
-  a.b = (mode == bd::MODE_CAUSAL) ? 1 : b;
-  a.mode = mode;
-  a.T = (mode == bd::MODE_CAUSAL) ? n : 2 * n;
-  a.nhalves = (mode == bd::MODE_CAUSAL) ? 1 : 2;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = p.B;
+  a.H = p.H;
+  a.Hkv = p.Hkv;
+  a.G = p.H / p.Hkv;
+  a.S = 1;
+  a.n = p.n;
+  a.b = (p.mode == bd::MODE_CAUSAL) ? 1 : p.b;
+  a.mode = p.mode;
+  a.T = p.T();
+  a.nhalves = (p.mode == bd::MODE_CAUSAL) ? 1 : 2;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.cu = p.cu;
+  a.tokens = p.tokens();
+  a.stat_hs = p.packed() ? p.total : p.T();
   return a;
 }
 
-int fwd_common(int mode, const void* q, const void* k, const void* v, void* out, float* lse,
-               int B, int n, int H, int H_kv, int D, int b, float scale, void* stream) {
+int run_fwd(const Problem& p, const void* q, const void* k, const void* v, void* out, float* lse,
+            void* stream) {
   if (!q || !k || !v || !out || !lse) return BDATTN_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 16))
     return BDATTN_ERR_INVALID;
-  if (n < 1 || b < 1) return BDATTN_ERR_INVALID;
-  if (mode == bd::MODE_DIFFUSION && n > std::numeric_limits<int>::max() / 2) return BDATTN_ERR_INVALID;
-  int st = check_shape(B, mode == bd::MODE_CAUSAL ? n : 2 * n, H, D);
+  const int st = check_problem(p);
   if (st != BDATTN_OK) return st;
-  if ((st = check_kv_heads(H, H_kv)) != BDATTN_OK) return st;
-  if ((st = check_scale(scale)) != BDATTN_OK) return st;
-  bd::AttnArgs a = make_args(mode, B, n, H, H_kv, b, scale);
+  bd::AttnArgs a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  hipError_t e = bd::launch_fwd(a, D, static_cast<hipStream_t>(stream));
+  hipError_t e = bd::launch_fwd(a, p.D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
 }
 
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
-// Backward workspace: -delta and lse2 per query row ([B][H][T] float32
-// each), then, when the dK/dV kernel splits the groups of query heads
-// (S > 1), float32 partial dK and dV ([S][B][T][H_kv][D] each).
-size_t stats_bytes(int B, int T, int H) { return round256(2 * (size_t)B * H * T * sizeof(float)); }
-
-int splits_of(int mode, int B, int n, int H, int H_kv) {
-  return bd::dkdv_group_splits(B, n, mode == bd::MODE_CAUSAL ? 1 : 2, H_kv, H / H_kv);
-}
-
-size_t workspace_bytes(int mode, int B, int n, int H, int H_kv, int D) {
-  if (n < 1 || (mode == bd::MODE_DIFFUSION && n > std::numeric_limits<int>::max() / 2)) return 0;
-  const int T = (mode == bd::MODE_CAUSAL) ? n : 2 * n;
-  if (check_shape(B, T, H, D) != BDATTN_OK || check_kv_heads(H, H_kv) != BDATTN_OK) return 0;
-  const int S = splits_of(mode, B, n, H, H_kv);
-  const size_t part = S > 1 ? 2 * (size_t)S * B * T * H_kv * D * sizeof(float) : 0;
-  return stats_bytes(B, T, H) + round256(part);
-}
-
-int bwd_common(int mode, int stage, const void* q, const void* k, const void* v, const void* out,
-               const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int n,
-               int H, int H_kv, int D, int b, float scale, void* workspace, size_t ws_bytes,
-               void* stream) {
+// stage < 0: the whole backward
+int run_bwd(const Problem& p, int stage, const void* q, const void* k, const void* v,
+            const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+            void* workspace, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
     return BDATTN_ERR_INVALID;
   const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return BDATTN_ERR_INVALID;
-  if (n < 1 || b < 1) return BDATTN_ERR_INVALID;
-  if (mode == bd::MODE_DIFFUSION && n > std::numeric_limits<int>::max() / 2) return BDATTN_ERR_INVALID;
-  const int T = (mode == bd::MODE_CAUSAL) ? n : 2 * n;
-  int st = check_shape(B, T, H, D);
+  for (const void* ptr : ptrs)
+    if (!aligned(ptr, 16)) return BDATTN_ERR_INVALID;
+  const int st = check_problem(p);
   if (st != BDATTN_OK) return st;
-  if ((st = check_kv_heads(H, H_kv)) != BDATTN_OK) return st;
-  if ((st = check_scale(scale)) != BDATTN_OK) return st;
-  if (ws_bytes < workspace_bytes(mode, B, n, H, H_kv, D)) return BDATTN_ERR_INVALID;
-  bd::AttnArgs a = make_args(mode, B, n, H, H_kv, b, scale);
-  a.S = splits_of(mode, B, n, H, H_kv);
+  if (ws_bytes < workspace_bytes(p)) return BDATTN_ERR_INVALID;
+  bd::AttnArgs a = make_args(p);
+  a.S = splits_of(p);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -126,15 +133,24 @@ int bwd_common(int mode, int stage, const void* q, const void* k, const void* v,
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse_in = lse;
   a.ndelta = static_cast<float*>(workspace);
-  a.lse2 = a.ndelta + (size_t)B * H * T;
-  a.part = a.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(B, T, H))
+  a.lse2 = a.ndelta + (size_t)p.tokens() * p.H;
+  a.part = a.S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(p))
                    : nullptr;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  hipError_t e = (stage < 0) ? bd::launch_bwd(a, D, static_cast<hipStream_t>(stream))
-                             : bd::launch_bwd_stage(a, D, stage, static_cast<hipStream_t>(stream));
+  hipError_t e = (stage < 0) ? bd::launch_bwd(a, p.D, static_cast<hipStream_t>(stream))
+                             : bd::launch_bwd_stage(a, p.D, stage, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
+}
+
+Problem batched(int mode, int B, int n, int H, int H_kv, int D, int b, float scale) {
+  return Problem{mode, B, n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, nullptr, 0};
+}
+
+Problem packed(int mode, const int32_t* cu, int B, int max_n, int total, int H, int H_kv, int D,
+               int b, float scale) {
+  return Problem{mode, B, max_n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, cu, total};
 }
 
 bool geom_args_ok(int mode, int n, int b) {
@@ -155,86 +171,156 @@ const char* bdattn_status_string(int status) {
   }
 }
 
+// ---- batched, H_kv = H ----------------------------------------------------
+
 int diffusion_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                        int n, int H, int D, int block_size, float scale, void* stream) {
-  return fwd_common(bd::MODE_DIFFUSION, q, k, v, out, lse, B, n, H, H, D, block_size, scale,
-                    stream);
-}
-
-int diffusion_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
-                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
-                           void* stream) {
-  return fwd_common(bd::MODE_DIFFUSION, q, k, v, out, lse, B, n, H, H_kv, D, block_size, scale,
-                    stream);
+  return run_fwd(batched(bd::MODE_DIFFUSION, B, n, H, H, D, block_size, scale), q, k, v, out, lse,
+                 stream);
 }
 
 size_t diffusion_attn_bwd_workspace_size(int B, int n, int H, int D) {
-  return workspace_bytes(bd::MODE_DIFFUSION, B, n, H, H, D);
-}
-
-size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D) {
-  return workspace_bytes(bd::MODE_DIFFUSION, B, n, H, H_kv, D);
+  return workspace_bytes(batched(bd::MODE_DIFFUSION, B, n, H, H, D, 1, 1.f));
 }
 
 int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                        int n, int H, int D, int block_size, float scale, void* workspace,
                        size_t workspace_bytes_, void* stream) {
-  return bwd_common(bd::MODE_DIFFUSION, -1, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H, D,
-                    block_size, scale, workspace, workspace_bytes_, stream);
-}
-
-int diffusion_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
-                           int n, int H, int H_kv, int D, int block_size, float scale,
-                           void* workspace, size_t workspace_bytes_, void* stream) {
-  return bwd_common(bd::MODE_DIFFUSION, -1, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
-                    block_size, scale, workspace, workspace_bytes_, stream);
+  return run_bwd(batched(bd::MODE_DIFFUSION, B, n, H, H, D, block_size, scale), -1, q, k, v, out,
+                 dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                     int S, int H, int D, float scale, void* stream) {
-  return fwd_common(bd::MODE_CAUSAL, q, k, v, out, lse, B, S, H, H, D, 1, scale, stream);
-}
-
-int causal_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                        int S, int H, int H_kv, int D, float scale, void* stream) {
-  return fwd_common(bd::MODE_CAUSAL, q, k, v, out, lse, B, S, H, H_kv, D, 1, scale, stream);
+  return run_fwd(batched(bd::MODE_CAUSAL, B, S, H, H, D, 1, scale), q, k, v, out, lse, stream);
 }
 
 size_t causal_attn_bwd_workspace_size(int B, int S, int H, int D) {
-  return workspace_bytes(bd::MODE_CAUSAL, B, S, H, H, D);
-}
-
-size_t causal_attn_bwd_gqa_workspace_size(int B, int S, int H, int H_kv, int D) {
-  return workspace_bytes(bd::MODE_CAUSAL, B, S, H, H_kv, D);
+  return workspace_bytes(batched(bd::MODE_CAUSAL, B, S, H, H, D, 1, 1.f));
 }
 
 int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B, int S,
                     int H, int D, float scale, void* workspace, size_t workspace_bytes_,
                     void* stream) {
-  return bwd_common(bd::MODE_CAUSAL, -1, q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H, D, 1,
-                    scale, workspace, workspace_bytes_, stream);
+  return run_bwd(batched(bd::MODE_CAUSAL, B, S, H, H, D, 1, scale), -1, q, k, v, out, dout, lse, dq,
+                 dk, dv, workspace, workspace_bytes_, stream);
+}
+
+// ---- batched, grouped heads -----------------------------------------------
+
+int diffusion_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* stream) {
+  return run_fwd(batched(bd::MODE_DIFFUSION, B, n, H, H_kv, D, block_size, scale), q, k, v, out,
+                 lse, stream);
+}
+
+size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D) {
+  return workspace_bytes(batched(bd::MODE_DIFFUSION, B, n, H, H_kv, D, 1, 1.f));
+}
+
+int diffusion_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                           int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* workspace, size_t workspace_bytes_, void* stream) {
+  return run_bwd(batched(bd::MODE_DIFFUSION, B, n, H, H_kv, D, block_size, scale), -1, q, k, v,
+                 out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+int causal_attn_fwd_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                        int S, int H, int H_kv, int D, float scale, void* stream) {
+  return run_fwd(batched(bd::MODE_CAUSAL, B, S, H, H_kv, D, 1, scale), q, k, v, out, lse, stream);
+}
+
+size_t causal_attn_bwd_gqa_workspace_size(int B, int S, int H, int H_kv, int D) {
+  return workspace_bytes(batched(bd::MODE_CAUSAL, B, S, H, H_kv, D, 1, 1.f));
 }
 
 int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* out,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                         int S, int H, int H_kv, int D, float scale, void* workspace,
                         size_t workspace_bytes_, void* stream) {
-  return bwd_common(bd::MODE_CAUSAL, -1, q, k, v, out, dout, lse, dq, dk, dv, B, S, H, H_kv, D, 1,
-                    scale, workspace, workspace_bytes_, stream);
+  return run_bwd(batched(bd::MODE_CAUSAL, B, S, H, H_kv, D, 1, scale), -1, q, k, v, out, dout, lse,
+                 dq, dk, dv, workspace, workspace_bytes_, stream);
 }
+
+// ---- packed variable-length samples -----------------------------------------
+// total_tokens = 0: nothing to compute (BDATTN_OK, nothing launched).
+
+int diffusion_attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              const int32_t* cu_seqlens, int B, int max_n, int total_tokens, int H,
+                              int H_kv, int D, int block_size, float scale, void* stream) {
+  if (total_tokens == 0) return BDATTN_OK;
+  if (!cu_seqlens) return BDATTN_ERR_INVALID;
+  return run_fwd(packed(bd::MODE_DIFFUSION, cu_seqlens, B, max_n, total_tokens, H, H_kv, D,
+                        block_size, scale),
+                 q, k, v, out, lse, stream);
+}
+
+size_t diffusion_attn_varlen_bwd_workspace_size(int B, int max_n, int total_tokens, int H, int H_kv,
+                                                int D) {
+  if (total_tokens == 0) return 0;
+  // the offsets are not read here; any aligned non-null stand-in will do
+  static const int32_t stand_in = 0;
+  return workspace_bytes(packed(bd::MODE_DIFFUSION, &stand_in, B, max_n, total_tokens, H, H_kv, D,
+                                1, 1.f));
+}
+
+int diffusion_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens, int B, int max_n, int total_tokens, int H,
+                              int H_kv, int D, int block_size, float scale, void* workspace,
+                              size_t workspace_bytes_, void* stream) {
+  if (total_tokens == 0) return BDATTN_OK;
+  if (!cu_seqlens) return BDATTN_ERR_INVALID;
+  return run_bwd(packed(bd::MODE_DIFFUSION, cu_seqlens, B, max_n, total_tokens, H, H_kv, D,
+                        block_size, scale),
+                 -1, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+int causal_attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* cu_seqlens, int B, int max_S, int total_tokens, int H,
+                           int H_kv, int D, float scale, void* stream) {
+  if (total_tokens == 0) return BDATTN_OK;
+  if (!cu_seqlens) return BDATTN_ERR_INVALID;
+  return run_fwd(packed(bd::MODE_CAUSAL, cu_seqlens, B, max_S, total_tokens, H, H_kv, D, 1, scale),
+                 q, k, v, out, lse, stream);
+}
+
+size_t causal_attn_varlen_bwd_workspace_size(int B, int max_S, int total_tokens, int H, int H_kv,
+                                             int D) {
+  if (total_tokens == 0) return 0;
+  static const int32_t stand_in = 0;
+  return workspace_bytes(packed(bd::MODE_CAUSAL, &stand_in, B, max_S, total_tokens, H, H_kv, D, 1,
+                                1.f));
+}
+
+int causal_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           const int32_t* cu_seqlens, int B, int max_S, int total_tokens, int H,
+                           int H_kv, int D, float scale, void* workspace, size_t workspace_bytes_,
+                           void* stream) {
+  if (total_tokens == 0) return BDATTN_OK;
+  if (!cu_seqlens) return BDATTN_ERR_INVALID;
+  return run_bwd(packed(bd::MODE_CAUSAL, cu_seqlens, B, max_S, total_tokens, H, H_kv, D, 1, scale),
+                 -1, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+// ---- one backward stage -----------------------------------------------------
 
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
-                     void* dv, int B, int n, int H, int H_kv, int D, int block_size, float scale,
-                     void* workspace, size_t workspace_bytes_, void* stream) {
+                     void* dv, const int32_t* cu_seqlens, int B, int n, int total_tokens, int H,
+                     int H_kv, int D, int block_size, float scale, void* workspace,
+                     size_t workspace_bytes_, void* stream) {
   if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
   if (stage < 0 || stage > 1) return BDATTN_ERR_INVALID;
-  return bwd_common(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, B, n, H, H_kv, D,
-                    mode == bd::MODE_CAUSAL ? 1 : block_size, scale, workspace, workspace_bytes_,
-                    stream);
+  const Problem p = cu_seqlens ? packed(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size,
+                                        scale)
+                               : batched(mode, B, n, H, H_kv, D, block_size, scale);
+  return run_bwd(p, stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
 static int list_tiles(bool fwd, int mode, int n, int block_size, int tile_m, int tile_n, int half,

@@ -43,8 +43,9 @@
 
 namespace bd {
 
-__device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
-  return (a.mode == MODE_DIFFUSION && half == CLEAN) ? a.n : 0;
+// Token offset of a half inside its sample (n: the sample's half length).
+__device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
+  return (a.mode == MODE_DIFFUSION && half == CLEAN) ? n : 0;
 }
 
 // Per-segment scalars.  A key-stationary wave needs, for each query half it
@@ -56,7 +57,7 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
 // selects: grouped in a struct, the compiler would select between the
 // structs' addresses and keep both in scratch memory.
 #define COL_SEGMENTS                                                          \
-  const size_t stat_base = ((size_t)bi * a.H + hh0) * a.T;                   \
+  const size_t stat_base = stat0 + (size_t)hh0 * a.stat_hs;                  \
   int clo_f0, chi_f0, clo_l0, chi_l0, clo_p0, chi_p0;                        \
   int clo_f1, chi_f1, clo_l1, chi_l1, clo_p1, chi_p1;                        \
   col_interval(g, seg.half0, kh, kw0, clo_f0, chi_f0);                        \
@@ -65,10 +66,10 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
   col_interval(g, seg.half1, kh, kw0, clo_f1, chi_f1);                        \
   col_interval(g, seg.half1, kh, max(kw1 - 1, kw0), clo_l1, chi_l1);          \
   col_interval(g, seg.half1, kh, key, clo_p1, chi_p1);                        \
-  const size_t qb0 = (sample0 + half_off(a, seg.half0)) * rs + (size_t)hh0 * D; \
-  const size_t qb1 = (sample0 + half_off(a, seg.half1)) * rs + (size_t)hh0 * D; \
-  const size_t sb0 = stat_base + half_off(a, seg.half0);                      \
-  const size_t sb1 = stat_base + half_off(a, seg.half1);
+  const size_t qb0 = (sample0 + half_off(a, seg.half0, n)) * rs + (size_t)hh0 * D; \
+  const size_t qb1 = (sample0 + half_off(a, seg.half1, n)) * rs + (size_t)hh0 * D; \
+  const size_t sb0 = stat_base + half_off(a, seg.half0, n);                   \
+  const size_t sb1 = stat_base + half_off(a, seg.half1, n);
 
 #define ROW_SEGMENTS                                                           \
   int lo_f0, hi_f0, lo_l0, hi_l0, lo_p0, hi_p0, lo_f1, hi_f1, lo_l1, hi_l1, lo_p1, hi_p1; \
@@ -78,8 +79,8 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half) {
   row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);                            \
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);              \
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);                              \
-  const size_t kvb0 = (sample0 + half_off(a, seg.half0)) * rs_kv + (size_t)hk * D; \
-  const size_t kvb1 = (sample0 + half_off(a, seg.half1)) * rs_kv + (size_t)hk * D;
+  const size_t kvb0 = (sample0 + half_off(a, seg.half0, n)) * rs_kv + (size_t)hk * D; \
+  const size_t kvb1 = (sample0 + half_off(a, seg.half1, n)) * rs_kv + (size_t)hk * D;
 
 // ---------------------------------------------------------------------------
 // dK / dV: key-stationary, one workgroup per 128 keys, 8 waves in 4 pairs.
@@ -154,26 +155,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const int hk = bh / S % a.Hkv;
   const int gs = GROUPED ? a.G / S : 1;         // query heads walked by this workgroup
   const int hh0 = GROUPED ? hk * a.G + split * gs : hk;  // the first of them
-  const Geom g{a.n, a.b};
+  size_t sample0, stat0;
+  int n;
+  // packed samples shorter than the longest leave their last tiles empty
+  if (!sample_of(a, bi, sample0, n, stat0) || kt * C::BKV >= n) return;
+  const Geom g{n, a.b};
   // Q / dO rows hold H heads, K / V / dK / dV rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
   const size_t rs_kv = (size_t)a.Hkv * D;
-  const size_t sample0 = (size_t)bi * a.T;
   const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t half_bytes = (uint32_t)n * row_bytes;
   const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
-  const size_t koff = sample0 + half_off(a, kh);
+  const size_t koff = sample0 + half_off(a, kh, n);
 
   const int kw0 = kt * C::BKV + 32 * pair;  // the pair's first key
-  const int kw1 = min(kw0 + 32, a.n);
-  const bool pair_active = kw0 < a.n;
+  const int kw1 = min(kw0 + 32, n);
+  const bool pair_active = kw0 < n;
   const int key = kw0 + l32;
 
   // The P-wave holds K, the dS-wave V, as B operands.
   bf16x8 xf[C::KS];
   {
     const rsrc_t rx = make_rsrc((pwave ? a.k : a.v) + koff * rs_kv + (size_t)hk * D,
-                                (uint32_t)a.n * kv_row_bytes);
+                                (uint32_t)n * kv_row_bytes);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
       xf[s] = as_bf16x8(buf_ld16(rx, (uint32_t)key * kv_row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u, 0));
@@ -194,13 +198,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     const bool second = i >= n0;
     const int qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
     const size_t qb = (second ? qb1 : qb0) + (size_t)gi * D;
-    const size_t sb = (second ? sb1 : sb0) + (size_t)gi * a.T;
+    const size_t sb = (second ? sb1 : sb0) + (size_t)gi * a.stat_hs;
     const uint32_t dst = sbase + (uint32_t)(buf * C::BUF) * 2u;
     Tile::load(make_rsrc(a.q + qb, half_bytes), row_bytes, qt * C::BQ, dst, tid);
     Tile::load(make_rsrc(a.dout + qb, half_bytes), row_bytes, qt * C::BQ, dst + Tile::ELEMS * 2u, tid);
     // rows past the half read lse2 = -delta = 0; their Q and dO rows are
     // zero too, so they add nothing to dV or dK
-    const uint32_t sbytes = (uint32_t)a.n * 4u;
+    const uint32_t sbytes = (uint32_t)n * 4u;
     const uint32_t fdst = fbase + (uint32_t)(buf * C::FBUF) * 4u;
     if (wv == 0)
       lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fdst, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
         const int r0 = qt * C::BQ + 32 * qb;
-        const int r1 = min(r0 + 32, a.n);
-        act[qb] = pair_active && r0 < a.n && r1 > cf && r0 < hl;
+        const int r1 = min(r0 + 32, n);
+        act[qb] = pair_active && r0 < n && r1 > cf && r0 < hl;
         full[qb] = r0 >= cl && r1 <= hf;
       }
     };
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     walk(std::false_type{});
 
   // lane = key, register r of block db = dimension 32db + 8(r/4) + 4h2 + r%4
-  if (pair_active && key < a.n) {
+  if (pair_active && key < n) {
     const size_t off = (koff + key) * rs_kv + (size_t)hk * D;
     const float f = pwave ? 1.f : a.scale;
     if (S == 1) {
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
         }
     } else {
       // float32 partial of this split: [S][B][T][Hkv][D], dK then dV
-      const size_t E = (size_t)a.B * a.T * a.Hkv * D;
+      const size_t E = (size_t)a.tokens * a.Hkv * D;
       float* dst = a.part + (pwave ? (size_t)S * E : 0) + (size_t)split * E + off;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -470,14 +474,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 // dK and dV of split groups: the sum of the S float32 partials, in split
 // order, rounded to bf16.  Each thread produces 8 consecutive elements of
 // the [B][T][Hkv][D] outputs; elements [0, E) are dK, [E, 2E) dV.
+// With packed samples (cu non-null) only the tokens [cu[0], cu[B]) belong
+// to samples: the other rows of dK and dV are left as they are.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                          uint16_t* __restrict__ dk,
                                                          uint16_t* __restrict__ dv, long long E,
-                                                         int S) {
+                                                         int S, const int* cu, int B, int row_elems) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= 2 * E) return;
   const bool second = i >= E;
   const long long e = second ? i - E : i;
+  if (cu != nullptr) {
+    const long long t = e / row_elems;
+    if (t < cu[0] || t >= cu[B]) return;
+  }
   const float* src = part + (second ? (long long)S * E : 0) + e;
   float4 lo = *reinterpret_cast<const float4*>(src);
   float4 hi = *reinterpret_cast<const float4*>(src + 4);
@@ -531,21 +541,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
   int bi, hh, hk;
   query_head(a, rr % BH, bi, hh, hk);
   const int qh = (a.mode == MODE_CAUSAL) ? CLEAN : half_idx;
-  const Geom g{a.n, a.b};
+  size_t sample0, stat0;
+  int n;
+  // packed samples shorter than the longest leave their last tiles empty
+  if (!sample_of(a, bi, sample0, n, stat0) || qt * C::BM >= n) return;
+  const Geom g{n, a.b};
   // Q / dO / O / dQ rows hold H heads, K / V rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
   const size_t rs_kv = (size_t)a.Hkv * D;
-  const size_t sample0 = (size_t)bi * a.T;
-  const int qoff = half_off(a, qh);
+  const int qoff = half_off(a, qh, n);
   const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t half_bytes = (uint32_t)n * row_bytes;
   const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
-  const uint32_t kv_half_bytes = (uint32_t)a.n * kv_row_bytes;
+  const uint32_t kv_half_bytes = (uint32_t)n * kv_row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
-  const int pw1 = min(pw0 + 32, a.n);
-  const bool wave_active = pw0 < a.n;
+  const int pw1 = min(pw0 + 32, n);
+  const bool wave_active = pw0 < n;
   const int p = pw0 + l32;
 
   // Q and dO as B operands: lane (row p, half h2) holds 16-byte chunks
@@ -572,8 +585,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
       gf[s] = as_bf16x8(buf_ld16(rg, off, 0));
       ov[s] = buf_ld16(ro, off, 0);
     }
-    const size_t sb = ((size_t)bi * a.H + hh) * a.T + qoff;
-    const float lse = buf_ldf(make_rsrc(a.lse_in + sb, (uint32_t)a.n * 4u), (uint32_t)p * 4u);
+    const size_t sb = stat0 + (size_t)hh * a.stat_hs + qoff;
+    const float lse = buf_ldf(make_rsrc(a.lse_in + sb, (uint32_t)n * 4u), (uint32_t)p * 4u);
     float dpart = 0.f;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
@@ -586,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
     }
     ndlt = -halves_sum(dpart);
     lse2 = lse * kLog2e;
-    if (wave_active && p < a.n && h2 == 0) {
+    if (wave_active && p < n && h2 == 0) {
       a.ndelta[sb + p] = ndlt;
       a.lse2[sb + p] = lse2;
     }
@@ -706,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
     if (i + 1 < ntiles) tile(std::integral_constant<int, 1>{}, i + 1);
   }
 
-  if (wave_active && p < a.n) {
+  if (wave_active && p < n) {
     uint16_t* qrow = a.dq + (sample0 + qoff + p) * rs + (size_t)hh * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -736,10 +749,10 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
     if (a.S > 1) {
-      const long long E = (long long)a.B * a.T * a.Hkv * D;
+      const long long E = a.tokens * a.Hkv * D;
       const long long rblocks = (2 * E / 8 + 255) / 256;
       hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, s, a.part, a.dk,
-                         a.dv, E, a.S);
+                         a.dv, E, a.S, a.cu, a.B, a.Hkv * D);
     }
   }
   return hipGetLastError();

@@ -52,8 +52,9 @@ struct FwdCfg {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-__device__ __forceinline__ int half_offset(const AttnArgs& a, int half) {
-  return (a.mode == MODE_DIFFUSION && half == CLEAN) ? a.n : 0;
+// Token offset of a half inside its sample (n: the sample's half length).
+__device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
+  return (a.mode == MODE_DIFFUSION && half == CLEAN) ? n : 0;
 }
 
 template <int D, int BN, int NW, int NBUF>
@@ -82,22 +83,25 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
   int bi, hh, hk;
   query_head(a, rr % BH, bi, hh, hk);
   const int qh = (a.mode == MODE_CAUSAL) ? CLEAN : half_idx;
-  const Geom g{a.n, a.b};
+  size_t sample0, stat0;
+  int n;
+  // packed samples shorter than the longest leave their last tiles empty
+  if (!sample_of(a, bi, sample0, n, stat0) || qt * C::BM >= n) return;
+  const Geom g{n, a.b};
 
   // Q / O rows hold H heads, K / V rows Hkv heads.
   const size_t rs = (size_t)a.H * D;
   const size_t rs_kv = (size_t)a.Hkv * D;
-  const size_t sample0 = (size_t)bi * a.T;
-  const int qoff = half_offset(a, qh);
+  const int qoff = half_offset(a, qh, n);
   const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const uint32_t half_bytes = (uint32_t)a.n * row_bytes;
+  const uint32_t half_bytes = (uint32_t)n * row_bytes;
   const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
-  const uint32_t kv_half_bytes = (uint32_t)a.n * kv_row_bytes;
+  const uint32_t kv_half_bytes = (uint32_t)n * kv_row_bytes;
 
   const int q0 = qt * C::BM;
   const int pw0 = q0 + 32 * w;
-  const int pw1 = min(pw0 + 32, a.n);
-  const bool wave_active = pw0 < a.n;
+  const int pw1 = min(pw0 + 32, n);
+  const bool wave_active = pw0 < n;
   const int p = pw0 + l32;
 
   // Q^T operand: lane (row p, half h2) holds Q[p][16s + 8h2 .. +7]; rows past
@@ -134,8 +138,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
   row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);
-  const size_t kvb0 = (sample0 + half_offset(a, seg.half0)) * rs_kv + (size_t)hk * D;
-  const size_t kvb1 = (sample0 + half_offset(a, seg.half1)) * rs_kv + (size_t)hk * D;
+  const size_t kvb0 = (sample0 + half_offset(a, seg.half0, n)) * rs_kv + (size_t)hk * D;
+  const size_t kvb1 = (sample0 + half_offset(a, seg.half1, n)) * rs_kv + (size_t)hk * D;
 
   auto issue_tile = [&](int i, int buf) __attribute__((always_inline)) {
     const bool second = i >= n0;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
 
   // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = halves_sum(l_run);
-  if (wave_active && p < a.n) {
+  if (wave_active && p < n) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = a.out + (sample0 + qoff + p) * rs + (size_t)hh * D;
 #pragma unroll
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
         *reinterpret_cast<u32x2*>(orow + d) = pk;
       }
     if (h2 == 0)
-      a.lse[((size_t)bi * a.H + hh) * a.T + qoff + p] = (m_run + log2f(l_tot)) * kLn2;
+      a.lse[stat0 + (size_t)hh * a.stat_hs + qoff + p] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 

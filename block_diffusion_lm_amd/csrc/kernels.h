@@ -5,10 +5,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "geometry.h"
+
 namespace bd {
 
 struct AttnArgs {
-  // inputs, bf16: q [B][T][H][D], k and v [B][T][Hkv][D]
+  // inputs, bf16: q [B][T][H][D], k and v [B][T][Hkv][D] (packed samples:
+  // [total][H][D] and [total][Hkv][D])
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -16,7 +19,7 @@ struct AttnArgs {
   const uint16_t* dout;  // gradient of the output
   // forward outputs
   uint16_t* out;
-  float* lse;            // [B][H][T], natural log
+  float* lse;            // [B][H][T] (packed: [H][total]), natural log
   // backward
   const float* lse_in;   // [B][H][T]
   float* ndelta;         // workspace [B][H][T]: -(dout_i . out_i)
@@ -24,13 +27,18 @@ struct AttnArgs {
   uint16_t* dq;
   uint16_t* dk;   // [B][T][Hkv][D], like k
   uint16_t* dv;
+  // packed samples: B + 1 token offsets in device memory (sample b holds
+  // tokens [cu[b], cu[b+1])), or null for the batched layout
+  const int* cu;
+  long long tokens;   // tokens of all samples: B * T, or the packed total
+  long long stat_hs;  // distance between heads in lse and the statistics: T, or the total
   // shape
   int B, H;
   int Hkv;      // key/value heads; query head h reads key/value head h / G
   int G;        // H / Hkv, query heads per key/value head
   int S;        // dK/dV workgroups per group of query heads (divides G)
   float* part;  // S > 1: float32 partial dK then dV, each [S][B][T][Hkv][D]
-  int n;        // half length (diffusion) or sequence length (causal)
+  int n;        // half length (diffusion) or sequence length (causal); packed: the longest
   int b;        // block size (1 for causal)
   int mode;     // MODE_DIFFUSION / MODE_CAUSAL
   int T;        // tokens per sample: 2n or n
@@ -59,6 +67,30 @@ __device__ __forceinline__ void query_head(const AttnArgs& a, int x, int& bi, in
 // than a few workgroups per CU; then the smallest divisor of G that does
 // not.  Above 1 the workgroups write float32 partials that a reduction sums.
 int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G);
+
+// Sample bi: the token index of its first token, its half length n
+// (sequence length in causal mode) and the index of its statistics for
+// head 0, row 0.  Batched: tok0 = bi * T, n = a.n, stat0 = bi * H * T.
+// Packed: tok0 = stat0 = cu[bi] and n from cu[bi + 1] - cu[bi].  A packed
+// sample whose offsets are inconsistent (negative, decreasing, past the
+// packed total, an odd diffusion length, or a half longer than a.n) yields
+// false, and its workgroups do nothing, so no access leaves the tensors.
+__device__ __forceinline__ bool sample_of(const AttnArgs& a, int bi, size_t& tok0, int& n,
+                                          size_t& stat0) {
+  if (a.cu == nullptr) {
+    tok0 = (size_t)bi * a.T;
+    n = a.n;
+    stat0 = (size_t)bi * a.H * a.T;
+    return true;
+  }
+  const int c0 = a.cu[bi];
+  const int c1 = a.cu[bi + 1];
+  const int len = c1 - c0;
+  n = (a.mode == MODE_CAUSAL) ? len : len / 2;
+  tok0 = stat0 = (size_t)(c0 < 0 ? 0 : c0);
+  return c0 >= 0 && len >= 0 && (long long)c1 <= a.tokens &&
+         (a.mode == MODE_CAUSAL || (len & 1) == 0) && n <= a.n;
+}
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s);

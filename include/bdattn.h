@@ -98,10 +98,13 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One stage of the backward pass (same arguments as diffusion_attn_bwd_gqa and
- * causal_attn_bwd_gqa below, with their workspace; H_kv = H for plain
- * multi-head attention; mode 0 = diffusion with block_size, 1 = causal with
- * n = S and block_size ignored):
+ * One stage of the backward pass, for timing the kernels separately.  The
+ * arguments are those of the backward entry points below: cu_seqlens NULL
+ * for the batched layout (n = half length, or S; total_tokens ignored),
+ * non-NULL for packed samples (n = the longest, total_tokens as in the
+ * varlen entry points); H_kv = H for plain multi-head attention; mode 0 =
+ * diffusion with block_size, 1 = causal (block_size ignored); workspace as
+ * the matching *_workspace_size function gives.
  *   stage 0 -- dQ; it also writes the per-row -delta_i = -(dout_i . out_i)
  *              and lse_i * log2(e) to the workspace;
  *   stage 1 -- dK and dV (reads the workspace written by stage 0; with
@@ -112,8 +115,9 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
  */
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
-                     void* dv, int B, int n, int H, int H_kv, int D, int block_size,
-                     float scale, void* workspace, size_t workspace_bytes, void* stream);
+                     void* dv, const int32_t* cu_seqlens, int B, int n, int total_tokens, int H,
+                     int H_kv, int D, int block_size, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Causal yardstick forward: q, k, v, out [B][S][H][D] bf16, lse [B][H][S] fp32. */
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -168,6 +172,52 @@ int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void*
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
                         int B, int S, int H, int H_kv, int D, float scale,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed batches of samples of different lengths (Fast Diffusion
+ * Attention, "Hopper": varlen batches, as in supervised fine-tuning).
+ *   cu_seqlens : B + 1 int32 token offsets in device memory, 4-byte aligned
+ *                (read by the kernels, never by the host): sample b holds
+ *                the packed tokens [cu_seqlens[b], cu_seqlens[b+1]), laid
+ *                out [noisy n_b | clean n_b] (diffusion, 2 n_b tokens) or
+ *                as one sequence of S_b tokens (causal).  Samples may be
+ *                empty.
+ *   max_n      : the largest n_b (max_S: the largest S_b), >= 1; it sizes
+ *                the grid, whose workgroups past a sample's end exit at
+ *                once, heaviest tiles first.
+ *   total_tokens : packed tokens (rows of q); 0 computes nothing and
+ *                returns BDATTN_OK.
+ *   q, out, dout, dq : [total_tokens][H][D] bf16
+ *   k, v, dk, dv     : [total_tokens][H_kv][D] bf16 (grouped heads as above)
+ *   lse              : [H][total_tokens] fp32
+ * Each sample is computed exactly as the batched entry points compute it
+ * on that sample alone.  A sample whose offsets are inconsistent
+ * (negative, decreasing, past total_tokens, an odd diffusion length, or
+ * longer than max_n) is skipped and its outputs are undefined; nothing
+ * outside the tensors is accessed.  Rows outside every sample are not
+ * written.  The workspace sizes follow the rules of the grouped backward,
+ * with total_tokens rows.
+ */
+int diffusion_attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              const int32_t* cu_seqlens, int B, int max_n, int total_tokens,
+                              int H, int H_kv, int D, int block_size, float scale, void* stream);
+size_t diffusion_attn_varlen_bwd_workspace_size(int B, int max_n, int total_tokens, int H,
+                                                int H_kv, int D);
+int diffusion_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens, int B, int max_n, int total_tokens,
+                              int H, int H_kv, int D, int block_size, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int causal_attn_varlen_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* cu_seqlens, int B, int max_S, int total_tokens, int H,
+                           int H_kv, int D, float scale, void* stream);
+size_t causal_attn_varlen_bwd_workspace_size(int B, int max_S, int total_tokens, int H, int H_kv,
+                                             int D);
+int causal_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           const int32_t* cu_seqlens, int B, int max_S, int total_tokens, int H,
+                           int H_kv, int D, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Host-side inspection of the tile enumeration the kernels use (pure integer

@@ -84,7 +84,7 @@ def test_bwd_rejects(kw, want):
 def test_bwd_stage_rejects_unknown_stage(stage):
     # stage 0 is dQ (with the row statistics), stage 1 dK/dV; nothing else
     lib = bd.lib()
-    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), 1, 16, 1, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
+    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), None, 1, 16, 0, 1, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
 
 
 def test_causal_rejects():
@@ -121,7 +121,7 @@ def test_grouped_entry_points_reject_bad_kv_heads(H, H_kv):
     assert lib.causal_attn_fwd_gqa(*([FAKE] * 5), 1, 16, H, H_kv, 64, 0.125, None) == INVALID
     assert lib.causal_attn_bwd_gqa(*([FAKE] * 9), 1, 16, H, H_kv, 64, 0.125, FAKE, 1 << 20,
                                    None) == INVALID
-    assert lib.bdattn_bwd_stage(0, 0, *([FAKE] * 9), 1, 16, H, H_kv, 64, 4, 0.125, FAKE, 1 << 20,
+    assert lib.bdattn_bwd_stage(0, 0, *([FAKE] * 9), None, 1, 16, 0, H, H_kv, 64, 4, 0.125, FAKE, 1 << 20,
                                 None) == INVALID
 
 
@@ -181,3 +181,45 @@ def test_gqa_bwd_rejects_a_workspace_without_room_for_partials():
     assert bd.diffusion_attn_bwd_gqa_workspace_size(B, n, H, 1, D) > stats_only
     assert bd.lib().diffusion_attn_bwd_gqa(*([FAKE] * 9), B, n, H, 1, D, 4, 0.125, FAKE, stats_only,
                                            None) == INVALID
+
+
+def test_varlen_rejects_bad_arguments():
+    lib = bd.lib()
+    # (B, max_n, total, H, H_kv, D, b)
+    ok = (2, 16, 40, 4, 2, 64, 4)
+    fwd = lambda cu, *a: lib.diffusion_attn_varlen_fwd(*([FAKE] * 5), cu, *a, 0.125, None)
+    assert fwd(None, *ok) == INVALID                       # no offsets
+    assert fwd(FAKE + 2, *ok) == INVALID                   # misaligned offsets
+    assert fwd(FAKE, 2, 0, 40, 4, 2, 64, 4) == INVALID     # max_n = 0 with tokens
+    assert fwd(FAKE, 2, 16, -1, 4, 2, 64, 4) == INVALID    # negative total
+    assert fwd(FAKE, 0, 16, 40, 4, 2, 64, 4) == INVALID    # no samples
+    assert fwd(FAKE, 2, 16, 40, 4, 3, 64, 4) == INVALID    # H not a multiple of H_kv
+    assert fwd(FAKE, 2, 16, 40, 4, 2, 96, 4) == UNSUPPORTED
+    # all rows past the 32-bit row limit
+    assert fwd(FAKE, 2, 16, 2 ** 30, 4, 2, 64, 4) == INVALID
+    bwd = lambda cu, wsb, *a: lib.diffusion_attn_varlen_bwd(*([FAKE] * 9), cu, *a, 0.125, FAKE, wsb, None)
+    assert bwd(None, 1 << 30, *ok) == INVALID
+    assert bwd(FAKE, 16, *ok) == INVALID                   # workspace too small
+    assert lib.causal_attn_varlen_fwd(*([FAKE] * 5), None, 2, 16, 40, 4, 2, 64, 0.1, None) == INVALID
+
+
+def test_varlen_with_no_tokens_launches_nothing():
+    # nothing to compute: OK without touching any pointer (there is no GPU here)
+    lib = bd.lib()
+    assert lib.diffusion_attn_varlen_fwd(*([FAKE] * 5), FAKE, 3, 0, 0, 4, 2, 64, 4, 0.125, None) == OK
+    assert lib.diffusion_attn_varlen_bwd(*([FAKE] * 9), FAKE, 3, 0, 0, 4, 2, 64, 4, 0.125, FAKE, 0,
+                                         None) == OK
+    assert bd.diffusion_attn_varlen_bwd_workspace_size(3, 0, 0, 4, 2, 64) == 0
+
+
+def test_varlen_workspace_sizes():
+    # statistics per packed row and head; partials when the groups split,
+    # by the same rule as the batched layout with max_n standing for n
+    B, max_n, total, H, Hkv, D = 5, 300, 1234, 8, 2, 64
+    want, S = _expected_gqa_workspace(B, max_n, H, Hkv, D)
+    r256 = lambda x: -(-x // 256) * 256
+    part = 2 * S * total * Hkv * D * 4 if S > 1 else 0
+    assert bd.diffusion_attn_varlen_bwd_workspace_size(B, max_n, total, H, Hkv, D) == \
+        r256(2 * H * total * 4) + r256(part)
+    assert bd.diffusion_attn_varlen_bwd_workspace_size(B, max_n, total, H, H, D) == r256(2 * H * total * 4)
+    assert bd.causal_attn_varlen_bwd_workspace_size(B, max_n, total, 4, 4, 128) == r256(2 * 4 * total * 4)

@@ -26,7 +26,8 @@ import torch
 
 import oracle
 import block_diffusion_lm_amd as bd
-from workloads import GQA_WORKLOADS, WORKLOADS, make_causal_view, make_inputs, make_workload_inputs
+from workloads import (GQA_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, make_causal_view, make_inputs,
+                       make_varlen_inputs, make_varlen_workload_inputs, make_workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -278,11 +279,13 @@ def test_backward_stages_in_order_on_two_streams():
     done0 = torch.cuda.Event()
     torch.cuda.synchronize()
     with torch.cuda.stream(s1):
-        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, B, n, H, H, D, w.b, scale, ws, stream=s1)
+        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, ws,
+                            stream=s1)
         done0.record(s1)
     s2.wait_event(done0)
     with torch.cuda.stream(s2):
-        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, B, n, H, H, D, w.b, scale, ws, stream=s2)
+        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, ws,
+                            stream=s2)
     torch.cuda.synchronize()
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(t.cpu(), ref[name]), name
@@ -493,6 +496,175 @@ def test_grouped_autograd_wrapper():
     ref = run_grouped(q, k, v, do, 4, 0.125)
     tq, tk, tv = (x.to(dev).requires_grad_() for x in (q, k, v))
     out, lse = bd.diffusion_attn_func(tq, tk, tv, 4, softmax_scale=0.125, return_lse=True)
+    out.backward(do.to(dev))
+    assert torch.equal(out.detach().cpu(), ref["out"])
+    assert torch.equal(lse.cpu(), ref["lse"])
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert torch.equal(t.grad.cpu(), ref[name]), name
+
+
+# ---------------------------------------------------------------------------
+# Packed batches of samples of different lengths
+# ---------------------------------------------------------------------------
+
+def run_varlen(q, k, v, do, cu, max_n, b, scale, causal=False):
+    """Forward and backward through the varlen entry points; CPU results."""
+    dev = _dev()
+    total, H, D = q.shape
+    Hkv = k.shape[1]
+    B = len(cu) - 1
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+    # poisoned outputs: rows outside every sample must come back untouched
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((H, total), 7.0, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)
+    if causal:
+        bd.causal_attn_varlen_fwd(q, k, v, out, lse, cu_t, B, max_n, total, H, Hkv, D, scale)
+        wsb = bd.causal_attn_varlen_bwd_workspace_size(B, max_n, total, H, Hkv, D)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        bd.causal_attn_varlen_bwd(q, k, v, out, do, lse, dq, dk, dv, cu_t, B, max_n, total, H, Hkv, D,
+                                  scale, ws, wsb)
+    else:
+        bd.diffusion_attn_varlen_fwd(q, k, v, out, lse, cu_t, B, max_n, total, H, Hkv, D, b, scale)
+        wsb = bd.diffusion_attn_varlen_bwd_workspace_size(B, max_n, total, H, Hkv, D)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        bd.diffusion_attn_varlen_bwd(q, k, v, out, do, lse, dq, dk, dv, cu_t, B, max_n, total, H, Hkv,
+                                     D, b, scale, ws, wsb)
+    torch.cuda.synchronize()
+    res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    return {key: t.cpu() for key, t in res.items()}
+
+
+VARLEN_SMALL = [  # half lengths, H, H_kv, D, b
+    ([100, 0, 7, 129, 1, 300], 3, 3, 64, 16),
+    ([64, 250, 0, 0, 33], 4, 2, 128, 5),
+    ([1, 2, 3, 200], 6, 1, 64, 200),
+    ([128, 384, 127, 129], 2, 2, 128, 32),
+]
+
+
+@pytest.mark.parametrize("ns,H,Hkv,D,b", VARLEN_SMALL)
+def test_varlen_small(ns, H, Hkv, D, b):
+    """Mixed lengths, empty samples, ragged tiles: against the oracle on every
+    sample; rows outside samples (none here) and no sample's rows are left
+    with the poison value."""
+    q, k, v, do, cu = make_varlen_inputs(ns, H, D, seed=9700 + sum(ns) + D, H_kv=Hkv)
+    scale = 1 / math.sqrt(D)
+    res = run_varlen(q, k, v, do, cu, max(ns), b, scale)
+    f = oracle.to_f64
+    O, L = oracle.varlen_forward(oracle.diffusion_forward, f(q), f(k), f(v), cu, b=b, scale=scale)
+    G = oracle.varlen_backward(oracle.diffusion_backward, f(q), f(k), f(v), f(do), cu, b=b, scale=scale)
+    tag = f"varlen {ns} H{H}/{Hkv} D{D} b{b}"
+    check_fwd(res["out"], res["lse"], O, L, tag)
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, tag)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_varlen_equals_batched_per_sample_bitwise(D):
+    """Each packed sample is computed exactly as the batched entry points
+    compute it alone (Fast Diffusion Attention, "Accuracy": the varlen
+    kernels agree with the batched ones), bit for bit; rows after the last
+    sample keep the caller's contents."""
+    ns, H, b = [300, 0, 129, 1, 64], 3, 16
+    q, k, v, do, cu = make_varlen_inputs(ns, H, D, seed=9800 + D)
+    pad = 5  # tokens after the last sample, in no sample
+    q, k, v, do = (torch.cat([x, torch.ones(pad, *x.shape[1:], dtype=x.dtype)]) for x in (q, k, v, do))
+    scale = 1 / math.sqrt(D)
+    res = run_varlen(q, k, v, do, cu, max(ns), b, scale)
+    for bi, nb in enumerate(ns):
+        if nb == 0:
+            continue
+        s0, s1 = cu[bi], cu[bi + 1]
+        one = run_diffusion(*(x[None, s0:s1] for x in (q, k, v, do)), b, scale)
+        for key in ("out", "dq", "dk", "dv"):
+            assert torch.equal(res[key][s0:s1], one[key][0]), (bi, key)
+        assert torch.equal(res["lse"][:, s0:s1], one["lse"][0]), bi
+    tail = slice(cu[-1], cu[-1] + pad)
+    for key in ("out", "dq", "dk", "dv"):
+        assert bool((res[key][tail] == 7.0).all()), key
+    assert bool((res["lse"][:, tail] == 7.0).all())
+
+
+@pytest.mark.parametrize("Hkv", [4, 2])
+def test_varlen_causal_small(Hkv):
+    ns, H, D = [150, 0, 77, 300], 4, 64
+    q, k, v, do, cu = make_varlen_inputs(ns, H, D, seed=9900 + Hkv, H_kv=Hkv, causal=True)
+    scale = 1 / math.sqrt(D)
+    res = run_varlen(q, k, v, do, cu, max(ns), 1, scale, causal=True)
+    f = oracle.to_f64
+    fwd = lambda qq, kk, vv, scale: oracle.causal_forward(qq, kk, vv, scale)
+    bwd = lambda qq, kk, vv, dd, scale: oracle.causal_backward(qq, kk, vv, dd, scale)
+    O, L = oracle.varlen_forward(fwd, f(q), f(k), f(v), cu, scale=scale)
+    G = oracle.varlen_backward(bwd, f(q), f(k), f(v), f(do), cu, scale=scale)
+    check_fwd(res["out"], res["lse"], O, L, f"causal varlen H{H}/{Hkv}")
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, f"causal varlen H{H}/{Hkv}")
+
+
+def test_varlen_skips_inconsistent_offsets():
+    """A sample whose offsets are inconsistent (here: an odd token count, and
+    one running past the packed total) is skipped by the kernels' own
+    checks; the consistent samples are still exact and nothing else is
+    written."""
+    H, D, b = 2, 64, 8
+    ns = [40, 30, 50]
+    q, k, v, do, cu = make_varlen_inputs(ns, H, D, seed=9950)
+    total = cu[-1]
+    scale = 1 / math.sqrt(D)
+    assert cu == [0, 80, 140, 240]
+    # sample 1 has an odd token count (59); sample 2 then covers tokens
+    # 139..239, a consistent 2 x 50
+    bad = [0, 80, 139, 239]
+    res = run_varlen(q, k, v, do, bad, 50, b, scale)
+    good = run_varlen(q, k, v, do, cu, 50, b, scale)
+    for key in ("out", "dq", "dk", "dv"):
+        assert torch.equal(res[key][:80], good[key][:80]), key
+        assert bool((res[key][80:139] == 7.0).all()), key
+        assert bool(torch.isfinite(res[key][139:239].float()).all()), key
+        assert bool((res[key][239:] == 7.0).all()), key
+    past = [0, 80, total + 64]                         # sample 1 ends past the tensors
+    res = run_varlen(q[:total], k[:total], v[:total], do[:total], past, 50, b, scale)
+    assert torch.equal(res["out"][:40 * 2], good["out"][:80])
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_WORKLOADS))
+def test_varlen_workloads(name):
+    """The packed workloads as the benchmark launches them: the longest and
+    the shortest sample of each, and one in between, checked on two heads."""
+    w = VARLEN_WORKLOADS[name]
+    q, k, v, do, cu = make_varlen_workload_inputs(w)
+    ns = w.half_lengths
+    scale = 1 / math.sqrt(w.D)
+    res = run_varlen(q, k, v, do, cu, max(ns), w.b, scale)
+    f = oracle.to_f64
+    G = w.H // w.kv_heads
+    order = sorted(range(len(ns)), key=lambda i: ns[i])
+    for bi in (order[-1], order[0], order[len(ns) // 2]):
+        s0, s1 = cu[bi], cu[bi + 1]
+        j = w.kv_heads - 1
+        hs = slice(j * G, (j + 1) * G)
+        sq, sdo = f(q[None, s0:s1, hs]), f(do[None, s0:s1, hs])
+        sk, sv = f(k[None, s0:s1, j:j + 1]), f(v[None, s0:s1, j:j + 1])
+        O, L = oracle.grouped_forward(oracle.diffusion_forward, sq, sk, sv, b=w.b, scale=scale)
+        dQ, dK, dV = oracle.grouped_backward(oracle.diffusion_backward, sq, sk, sv, sdo, b=w.b, scale=scale)
+        tag = f"{name} sample {bi} (n={ns[bi]}) kv head {j}"
+        check_fwd(res["out"][None, s0:s1, hs], res["lse"][hs, s0:s1][None], O, L, tag)
+        check_grad(res["dq"][None, s0:s1, hs], dQ, "dq", tag)
+        check_grad(res["dk"][None, s0:s1, j:j + 1], dK, "dk", tag)
+        check_grad(res["dv"][None, s0:s1, j:j + 1], dV, "dv", tag)
+
+
+def test_varlen_autograd_wrapper():
+    dev = _dev()
+    ns, H, Hkv, D = [70, 0, 33, 128], 4, 2, 64
+    q, k, v, do, cu = make_varlen_inputs(ns, H, D, seed=9990, H_kv=Hkv)
+    ref = run_varlen(q, k, v, do, cu, max(ns), 4, 0.125)
+    tq, tk, tv = (x.to(dev).requires_grad_() for x in (q, k, v))
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+    out, lse = bd.diffusion_attn_varlen_func(tq, tk, tv, cu_t, max(ns), 4, softmax_scale=0.125,
+                                             return_lse=True)
     out.backward(do.to(dev))
     assert torch.equal(out.detach().cpu(), ref["out"])
     assert torch.equal(lse.cpu(), ref["lse"])
