@@ -223,3 +223,11 @@ def test_varlen_workspace_sizes():
         r256(2 * H * total * 4) + r256(part)
     assert bd.diffusion_attn_varlen_bwd_workspace_size(B, max_n, total, H, H, D) == r256(2 * H * total * 4)
     assert bd.causal_attn_varlen_bwd_workspace_size(B, max_n, total, 4, 4, 128) == r256(2 * 4 * total * 4)
+
+
+def test_one_more_token_past_the_largest_sample_is_rejected():
+    # 2n x H x D bf16 must stay below 2 GiB: n = 16383 at H = 256, D = 128 is
+    # the largest accepted half (exercised on the GPU), n = 16384 is not
+    assert _fwd(n=16384, H=256, D=128) == UNSUPPORTED
+    assert bd.diffusion_attn_bwd_workspace_size(1, 16383, 256, 128) > 0
+    assert bd.diffusion_attn_bwd_workspace_size(1, 16384, 256, 128) == 0

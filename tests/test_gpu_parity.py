@@ -670,3 +670,38 @@ def test_varlen_autograd_wrapper():
     assert torch.equal(lse.cpu(), ref["lse"])
     for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
         assert torch.equal(t.grad.cpu(), ref[name]), name
+
+
+def test_largest_accepted_sample():
+    """The largest accepted sample: 2n tokens x 256 heads x D = 128 of bf16
+    just under 2 GiB (one more token per half is rejected), so every 32-bit
+    buffer offset is at its limit.  Checked on the last head: rows at the
+    ends of both halves for O, LSE and dQ, and key columns there for dK/dV."""
+    B, n, H, D, b = 1, 16383, 256, 128, 64
+    assert 2 * n * H * D * 2 < 2 ** 31 <= 2 * (n + 1) * H * D * 2
+    dev = _dev()
+    q, k, v, do = make_inputs(B, n, H, D, seed=9995)
+    scale = 1 / math.sqrt(D)
+    res = run_diffusion(q, k, v, do, b, scale)
+    hi = H - 1
+    f = lambda x: oracle.to_f64(x[0, :, hi])
+    qh, kh, vh, dh = f(q), f(k), f(v), f(do)
+    rows = np.array([0, 1, n - 2, n - 1, n, n + 1, 2 * n - 2, 2 * n - 1])
+    O, L = oracle.diffusion_forward_rows(qh, kh, vh, b, scale, rows)
+    check_fwd(res["out"][0, rows, hi], res["lse"][0, hi, rows], O, L, "largest sample")
+    check_grad(res["dq"][0, rows, hi], oracle.diffusion_grad_q_rows(qh, kh, vh, dh, b, scale, rows),
+               "dq", "largest sample")
+    # The last two keys of each half lie in its last block (63 keys) and are
+    # seen only by the rows of that block (no noisy row sees a clean key of
+    # the last block), so only
+    # those rows' statistics are needed; the others get probability 0 for
+    # these keys and are left at zero.
+    cols = np.array([n - 2, n - 1, 2 * n - 2, 2 * n - 1])
+    last = (n - 1) // b * b
+    seen = np.r_[last:n, n + last:2 * n]
+    Of = np.zeros((2 * n, D))
+    Lf = np.zeros(2 * n)
+    Of[seen], Lf[seen] = oracle.diffusion_forward_rows(qh, kh, vh, b, scale, seen)
+    dk_ref, dv_ref = oracle.diffusion_grad_kv_cols(qh, kh, vh, dh, Of, Lf, b, scale, cols)
+    check_grad(res["dk"][0, cols, hi], dk_ref, "dk", "largest sample")
+    check_grad(res["dv"][0, cols, hi], dv_ref, "dv", "largest sample")

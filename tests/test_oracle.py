@@ -516,3 +516,24 @@ def test_varlen_inputs_are_seeded_and_packed():
     q2, *_ = make_varlen_inputs(ns, 4, 8, seed=9, H_kv=2)
     assert torch.equal(q, q2)
     assert cu_seqlens(ns, causal=True) == [0, 3, 3, 8]
+
+
+@pytest.mark.parametrize("n,b", [(1000, 64), (130, 7), (64, 64), (16383, 64)])
+def test_last_keys_are_seen_only_by_the_last_block(n, b):
+    """When the last two keys of each half lie in its last block, they are
+    seen by the rows of that block (in the same half) and no others; the
+    full-size GPU test relies on this to need only those rows' statistics."""
+    assert (n - 1) // b == (n - 2) // b
+    if n > 2048:  # the two row blocks and key columns involved, not the whole mask
+        rows = np.r_[0:4 * b, n - 4 * b:n + 4 * b, 2 * n - 4 * b:2 * n]
+        M = oracle.block_diffusion_mask(n, b, rows)
+        last = (n - 1) // b * b
+        cols = np.array([n - 2, n - 1, 2 * n - 2, 2 * n - 1])
+        got = rows[M[:, cols].any(axis=1)]
+        assert np.array_equal(got, np.r_[last:n, n + last:2 * n])
+        return
+    cols = np.array([n - 2, n - 1, 2 * n - 2, 2 * n - 1])
+    last = (n - 1) // b * b
+    seen = np.r_[last:n, n + last:2 * n]
+    M = _prose_mask(n, b)
+    assert np.array_equal(np.flatnonzero(M[:, cols].any(axis=1)), seen)
