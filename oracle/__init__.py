@@ -32,3 +32,9 @@ from .attention import (  # noqa: F401
     batched,
     to_f64,
 )
+from .fp8 import (  # noqa: F401
+    dequantize_e4m3,
+    e4m3_value,
+    fp8_forward,
+    fp8_output_bound,
+)

@@ -17,7 +17,8 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from workloads import WORKLOADS, cu_seqlens, make_inputs, make_varlen_inputs
+from workloads import (WORKLOADS, cu_seqlens, make_fp8_inputs, make_fp8_integer_score_inputs, make_inputs,
+                       make_varlen_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -537,3 +538,104 @@ def test_last_keys_are_seen_only_by_the_last_block(n, b):
     seen = np.r_[last:n, n + last:2 * n]
     M = _prose_mask(n, b)
     assert np.array_equal(np.flatnonzero(M[:, cols].any(axis=1)), seen)
+
+
+# --------------------------------------------------------------------------
+# FP8 forward: the E4M3 decoder, dequantized attention, the error bound
+# --------------------------------------------------------------------------
+
+def test_e4m3_decoder_matches_the_format():
+    """Every code against torch's float8_e4m3fn (the same OCP format) and the
+    format's landmarks: 1.0, the largest finite value, the smallest normal
+    and subnormal values, the NaN patterns, signed zero."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    np.testing.assert_array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert oracle.e4m3_value(0x38) == 1.0 and oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    assert oracle.e4m3_value(0x80) == 0.0 and oracle.e4m3_value(0xC0) == -2.0
+
+
+def test_fp8_forward_is_attention_on_dequantized_values():
+    """The FP8 reference is exact attention over descale * value, with the
+    dequantization done here by torch's own cast."""
+    n, D, b, scale = 11, 16, 3, 0.3
+    q8, k8, v8, qd, kd, vd = make_fp8_inputs(1, n, 1, D, seed=80)
+    u8 = lambda t: t[0, :, 0].view(torch.uint8).numpy()
+    deq = lambda t, d: t[0, :, 0].to(torch.float64).numpy() * float(d[0, 0])
+    O, L = oracle.fp8_forward(u8(q8), u8(k8), u8(v8), float(qd[0, 0]), float(kd[0, 0]), float(vd[0, 0]), b, scale)
+    Or, Lr = oracle.diffusion_forward(deq(q8, qd), deq(k8, kd), deq(v8, vd), b, scale)
+    np.testing.assert_array_equal(O, Or)
+    np.testing.assert_array_equal(L, Lr)
+
+
+def _emulated_fp8_pv(q, k, v, b, scale, lag):
+    """O with P~ = exp2(s log2 e - m) rounded to E4M3 by torch, for a
+    reference m = row maximum - lag (lag < 8, as the lazy rescale allows)."""
+    n = q.shape[0] // 2
+    M = oracle.block_diffusion_mask(n, b)
+    s2 = np.where(M, scale * (q @ k.T) * math.log2(math.e), -np.inf)
+    m = s2.max(axis=1, keepdims=True) - lag
+    pt = np.exp2(s2 - m)
+    p8 = torch.from_numpy(pt).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return (p8 @ v) / pt.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("lag", [0.0, 3.7, 7.9])
+def test_fp8_output_bound_covers_the_rounding_of_p(lag):
+    """The bound holds for P~ actually rounded to E4M3 (by torch), whatever
+    the lazy reference's distance below the row maximum; and it is not
+    vacuous (the rounding error reaches a sizeable part of it)."""
+    n, D, b, scale = 40, 32, 5, 0.8
+    q8, k8, v8, qd, kd, vd = make_fp8_inputs(1, n, 1, D, seed=81)
+    deq = lambda t, d: t[0, :, 0].to(torch.float64).numpy() * float(d[0, 0])
+    q, k, v = deq(q8, qd), deq(k8, kd), deq(v8, vd)
+    O, _ = oracle.diffusion_forward(q, k, v, b, scale)
+    err = np.abs(_emulated_fp8_pv(q, k, v, b, scale, lag) - O)
+    bound = oracle.fp8_output_bound(q, k, v, b, scale)
+    assert np.all(err <= bound)
+    assert err.max() > 0.05 * bound.max()
+
+
+def test_fp8_integer_scores_make_p_exact():
+    """With integer base-2 scores (two +-1 entries per row of q and k,
+    scale = ln 2) every P~ is a power of two within E4M3's range, so the
+    rounded P.V equals exact attention up to float64 rounding."""
+    n, D, b = 24, 64, 4
+    q8, k8, v8, qd, kd, vd = make_fp8_integer_score_inputs(1, n, 1, D, seed=82)
+    deq = lambda t, d: t[0, :, 0].to(torch.float64).numpy() * float(d[0, 0])
+    q, k, v = deq(q8, qd), deq(k8, kd), deq(v8, vd)
+    scale = math.log(2.0)
+    s = q @ k.T
+    assert np.array_equal(s, np.round(s)) and np.abs(s).max() <= 2
+    O, _ = oracle.diffusion_forward(q, k, v, b, scale)
+    for lag in (0.0, 3.0):  # integer lags keep the powers of two
+        np.testing.assert_allclose(_emulated_fp8_pv(q, k, v, b, scale, lag), O, atol=1e-12)
+
+
+def test_fp8_output_bound_needs_its_subnormal_term():
+    """A row whose output comes from probabilities below E4M3's smallest
+    normal value (2^-6): one key at score 0 with value 0, the others at a
+    base-2 score of -7.3 with value 1.  Their rounding error (up to 2^-10
+    absolute, about 16% relative) exceeds the 2^-4 relative term alone; the
+    bound's second term covers it."""
+    n, b = 40, 40                  # row 0 sees exactly the 40 noisy keys
+    scale = 1.0 / math.log2(math.e)
+    q = np.zeros((2 * n, 2))
+    k = np.zeros((2 * n, 2))
+    v = np.zeros((2 * n, 2))
+    q[:, 0] = 1.0
+    k[1:n, 0] = -7.3
+    v[1:n, 0] = 1.0
+    O, _ = oracle.diffusion_forward(q, k, v, b, scale)
+    err = np.abs(_emulated_fp8_pv(q, k, v, b, scale, 0.0) - O)[0, 0]
+    bound = oracle.fp8_output_bound(q, k, v, b, scale, rows=[0])[0, 0]
+    M = oracle.block_diffusion_mask(n, b, [0])
+    s = np.where(M, scale * (q[[0]] @ k.T), -np.inf)
+    P = np.exp(s - s.max())
+    P /= P.sum()
+    assert err <= bound
+    assert err > 2.0 ** -4 * (P @ np.abs(v))[0, 0]

@@ -194,3 +194,45 @@ def make_varlen_inputs(half_lengths: Sequence[int], H: int, D: int, seed: int, H
 
 def make_varlen_workload_inputs(w: VarlenWorkload):
     return make_varlen_inputs(w.half_lengths, w.H, w.D, w.seed, H_kv=w.H_kv)
+
+
+def make_fp8_inputs(B: int, n: int, H: int, D: int, seed: int, H_kv: int = 0):
+    """FP8 (OCP E4M3) inputs of the FP8 forward pass and their descale factors.
+
+    Draws float32 N(0, 1) q (H heads), k and v (H_kv heads, 0: H) in that
+    order, then per (sample, head) descale exponents u in [-3, 1] for q, k,
+    v; each tensor is divided by 2^u and cast to float8_e4m3fn (torch's
+    round-to-nearest-even).  Returns (q8, k8, v8, q_descale [B][H],
+    k_descale [B][H_kv], v_descale [B][H_kv]), all CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    kv = H_kv or H
+    x = [torch.randn((B, 2 * n, h, D), generator=g, dtype=torch.float32) for h in (H, kv, kv)]
+    ds = [torch.exp2(torch.randint(-3, 2, (B, h), generator=g).to(torch.float32)) for h in (H, kv, kv)]
+    q8, k8, v8 = ((t / d[:, None, :, None]).to(torch.float8_e4m3fn) for t, d in zip(x, ds))
+    return q8, k8, v8, ds[0], ds[1], ds[2]
+
+
+def make_fp8_integer_score_inputs(B: int, n: int, H: int, D: int, seed: int, H_kv: int = 0):
+    """FP8 inputs whose scores are small integers: every row of q and k has
+    two entries of +-1 (descale 1), so q.k lies in [-2, 2]; v as in
+    ``make_fp8_inputs``.  With scale = ln 2 the scaled base-2 scores are
+    integers, so every unnormalised probability is a power of two (exact in
+    E4M3).  Returns the same six tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    kv = H_kv or H
+
+    def sparse(h):
+        t = torch.zeros((B, 2 * n, h, D), dtype=torch.float32)
+        rows = B * 2 * n * h
+        idx = torch.argsort(torch.rand((rows, D), generator=g), dim=1)[:, :2]  # two distinct columns
+        sgn = torch.randint(0, 2, (rows, 2), generator=g).to(torch.float32) * 2 - 1
+        t.view(-1, D).scatter_(1, idx, sgn)
+        return t.to(torch.float8_e4m3fn)
+
+    q8, k8 = sparse(H), sparse(kv)
+    v = torch.randn((B, 2 * n, kv, D), generator=g, dtype=torch.float32)
+    vd = torch.exp2(torch.randint(-3, 2, (B, kv), generator=g).to(torch.float32))
+    v8 = (v / vd[:, None, :, None]).to(torch.float8_e4m3fn)
+    return q8, k8, v8, torch.ones(B, H), torch.ones(B, kv), vd
