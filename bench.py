@@ -37,6 +37,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -62,6 +63,8 @@ def parse():
                     help="folder holding traffic_<kernel>_<workload>.txt (HBM bytes per launch)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 (E4M3) forward pass instead (batched workloads)")
     return ap.parse_args()
 
 
@@ -339,6 +342,93 @@ def setup_varlen(w, dev, torch, bd):
                            "headdim": D, "parallelism": "single-gpu"})
 
 
+def bench_fp8(args, w, dev, torch, bd):
+    """The FP8 forward on a batched workload: its rate, its FP8 causal
+    yardstick (interleaved rounds, medians) and the bf16 forward on the
+    same shapes."""
+    from workloads import make_fp8_inputs, make_workload_inputs
+    B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
+    scale = 1.0 / math.sqrt(D)
+    q8, k8, v8, qd, kd, vd = (x.to(dev) for x in make_fp8_inputs(B, n, H, D, w.seed, H_kv=w.H_kv))
+    out = torch.empty((B, 2 * n, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, 2 * n), dtype=torch.float32, device=dev)
+    cq, ck, cv = q8.view(2 * B, n, H, D), k8.view(2 * B, n, Hkv, D), v8.view(2 * B, n, Hkv, D)
+    cqd, ckd, cvd = (x.repeat_interleave(2, dim=0).contiguous() for x in (qd, kd, vd))
+    cout = torch.empty((2 * B, n, H, D), dtype=torch.bfloat16, device=dev)
+    clse = torch.empty((2 * B, H, n), dtype=torch.float32, device=dev)
+    q, k, v, _ = (x.to(dev) if x is not None else None for x in make_workload_inputs(w, with_dout=False))
+
+    def fp8_fwd():
+        bd.diffusion_attn_fwd_fp8(q8, k8, v8, qd, kd, vd, out, lse, B, n, H, Hkv, D, b, scale)
+
+    def fp8_causal():
+        bd.causal_attn_fwd_fp8(cq, ck, cv, cqd, ckd, cvd, cout, clse, 2 * B, n, H, Hkv, D, scale)
+
+    def bf16_fwd():
+        if Hkv == H:
+            bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
+        else:
+            bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for fn in (fp8_fwd, fp8_causal, bf16_fwd):
+        for _ in range(args.warmup):
+            fn()
+    torch.cuda.synchronize()
+    clock = ClockSampler()
+    clock.start()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fp8_fwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_event = timed(fp8_fwd, args.steps)
+    reps = max(1, int(math.ceil(args.round_ms / max(ms, 1e-3))))
+    rounds = {"fp8": [], "fp8_causal": [], "bf16": []}
+    for _ in range(args.rounds):
+        for name, fn in (("fp8", fp8_fwd), ("fp8_causal", fp8_causal), ("bf16", bf16_fwd)):
+            rounds[name].append(timed(fn, reps))
+    clock.stop()
+    med = {name: statistics.median(x) for name, x in rounds.items()}
+    P = visible_pairs(n, b)
+    F = 4.0 * P * D * H * B
+    Fc = 4.0 * (n * (n + 1) // 2) * D * H * 2 * B
+    tf = lambda F_, ms_: F_ / (ms_ * 1e-3) / 1e12
+    achieved = tf(F, ms_event)
+    return {
+        "metric": "FP8 forward TFLOPS (visible pairs only)",
+        "value": tf(F, ms),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "global_batch": B, "seq_len": 2 * n, "block_size": b,
+                   "heads": H, "kv_heads": Hkv, "headdim": D, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP8_TFLOPS, "traffic": None, "kernel": "fwd_fp8",
+                     "algorithmic_flops_per_launch": F, "avg_launch_ms": ms_event},
+        "interleaved_medians_ms": med,
+        "ratio_vs_causal": tf(F, med["fp8"]) / tf(Fc, med["fp8_causal"]),
+        "speedup_vs_bf16_forward": med["bf16"] / med["fp8"],
+        "device": torch.cuda.get_device_name(dev),
+        "sclk": clock.summary(),
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -363,6 +453,12 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.fp8:
+        if setup is not setup_batched:
+            print("--fp8 takes a batched workload", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(bench_fp8(args, w, dev, torch, bd)))
+        return
     prob = setup(w, dev, torch, bd)
     D = w.D
 

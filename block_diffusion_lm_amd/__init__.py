@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     causal_attn_bwd_gqa_workspace_size,
     causal_attn_bwd_workspace_size,
     causal_attn_fwd,
+    causal_attn_fwd_fp8,
     causal_attn_fwd_gqa,
     causal_attn_varlen_bwd,
     causal_attn_varlen_bwd_workspace_size,
@@ -30,6 +31,7 @@ from ._binding import (  # noqa: F401
     diffusion_attn_bwd_gqa_workspace_size,
     diffusion_attn_bwd_workspace_size,
     diffusion_attn_fwd,
+    diffusion_attn_fwd_fp8,
     diffusion_attn_fwd_gqa,
     diffusion_attn_varlen_bwd,
     diffusion_attn_varlen_bwd_workspace_size,

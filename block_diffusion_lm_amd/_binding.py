@@ -32,6 +32,8 @@ SIGNATURES = {
     "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 10 + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "diffusion_attn_fwd_fp8": (_i, [_vp] * 8 + [_i] * 6 + [_f, _vp]),
+    "causal_attn_fwd_fp8": (_i, [_vp] * 8 + [_i] * 5 + [_f, _vp]),
     "diffusion_attn_varlen_fwd": (_i, [_vp] * 6 + [_i] * 7 + [_f, _vp]),
     "diffusion_attn_varlen_bwd_workspace_size": (_sz, [_i] * 6),
     "diffusion_attn_varlen_bwd": (_i, [_vp] * 10 + [_i] * 7 + [_f, _vp, _sz, _vp]),
@@ -363,3 +365,34 @@ def bdattn_visible_pairs(mode, n, block_size) -> int:
     if r < 0:
         raise ValueError("bad geometry arguments")
     return int(r)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) forward: q [B][T][H][D], k / v [B][T][H_kv][D] as
+# torch.float8_e4m3fn, descale factors float32 [B][H] / [B][H_kv]
+# ---------------------------------------------------------------------------
+
+def _want_fwd_fp8(q, k, v, qd, kd, vd, out, lse, B, T, H, H_kv, D):
+    f8, f32 = torch.float8_e4m3fn, torch.float32
+    _want(("q", q, f8, (B, T, H, D)), ("k", k, f8, (B, T, H_kv, D)), ("v", v, f8, (B, T, H_kv, D)),
+          ("q_descale", qd, f32, (B, H)), ("k_descale", kd, f32, (B, H_kv)),
+          ("v_descale", vd, f32, (B, H_kv)), ("out", out, torch.bfloat16, (B, T, H, D)),
+          ("lse", lse, f32, (B, H, T)))
+
+
+def diffusion_attn_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, out, lse, B, n, H, H_kv, D,
+                           block_size, scale, stream=None):
+    _want_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, out, lse, B, 2 * n, H, H_kv, D)
+    _check(lib().diffusion_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
+                                        _ptr(v_descale), _ptr(out), _ptr(lse), B, n, H, H_kv, D,
+                                        block_size, float(scale), _stream_handle(q, stream)),
+           "diffusion_attn_fwd_fp8")
+
+
+def causal_attn_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, out, lse, B, S, H, H_kv, D, scale,
+                        stream=None):
+    _want_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, out, lse, B, S, H, H_kv, D)
+    _check(lib().causal_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
+                                     _ptr(v_descale), _ptr(out), _ptr(lse), B, S, H, H_kv, D,
+                                     float(scale), _stream_handle(q, stream)),
+           "causal_attn_fwd_fp8")

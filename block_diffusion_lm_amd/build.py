@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libbdattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip"]
 
 ARCH = "gfx950"
 

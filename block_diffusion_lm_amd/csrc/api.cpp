@@ -112,6 +112,27 @@ int run_fwd(const Problem& p, const void* q, const void* k, const void* v, void*
   return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
 }
 
+int run_fwd_fp8(const Problem& p, const void* q, const void* k, const void* v, const float* qd,
+                const float* kd, const float* vd, void* out, float* lse, void* stream) {
+  if (!q || !k || !v || !qd || !kd || !vd || !out || !lse) return BDATTN_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 16))
+    return BDATTN_ERR_INVALID;
+  if (!aligned(qd, 4) || !aligned(kd, 4) || !aligned(vd, 4)) return BDATTN_ERR_INVALID;
+  const int st = check_problem(p);
+  if (st != BDATTN_OK) return st;
+  bd::AttnArgs a = make_args(p);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.qd = qd;
+  a.kd = kd;
+  a.vd = vd;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  hipError_t e = bd::launch_fwd_fp8(a, p.D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
+}
+
 // stage < 0: the whole backward
 int run_bwd(const Problem& p, int stage, const void* q, const void* k, const void* v,
             const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -244,6 +265,23 @@ int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void*
                         size_t workspace_bytes_, void* stream) {
   return run_bwd(batched(bd::MODE_CAUSAL, B, S, H, H_kv, D, 1, scale), -1, q, k, v, out, dout, lse,
                  dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+// ---- FP8 (E4M3) forward -------------------------------------------------------
+
+int diffusion_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                           const float* k_descale, const float* v_descale, void* out, float* lse,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* stream) {
+  return run_fwd_fp8(batched(bd::MODE_DIFFUSION, B, n, H, H_kv, D, block_size, scale), q, k, v,
+                     q_descale, k_descale, v_descale, out, lse, stream);
+}
+
+int causal_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, const float* v_descale, void* out, float* lse,
+                        int B, int S, int H, int H_kv, int D, float scale, void* stream) {
+  return run_fwd_fp8(batched(bd::MODE_CAUSAL, B, S, H, H_kv, D, 1, scale), q, k, v, q_descale,
+                     k_descale, v_descale, out, lse, stream);
 }
 
 // ---- packed variable-length samples -----------------------------------------

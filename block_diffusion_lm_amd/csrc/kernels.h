@@ -24,6 +24,10 @@ struct AttnArgs {
   const float* lse_in;   // [B][H][T]
   float* ndelta;         // workspace [B][H][T]: -(dout_i . out_i)
   float* lse2;           // workspace [B][H][T]: lse * log2(e)
+  // FP8 forward: float32 descale factors of q [B][H], k and v [B][Hkv]
+  const float* qd;
+  const float* kd;
+  const float* vd;
   uint16_t* dq;
   uint16_t* dk;   // [B][T][Hkv][D], like k
   uint16_t* dv;
@@ -94,6 +98,8 @@ __device__ __forceinline__ bool sample_of(const AttnArgs& a, int bi, size_t& tok
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s);
+// q, k, v hold OCP E4M3 bytes (same layouts), with a.qd, a.kd, a.vd.
+hipError_t launch_fwd_fp8(const AttnArgs& a, int D, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, int D, hipStream_t s);
 // One backward stage: 0 = dQ (also writes -delta and lse2), 1 = dK/dV
 // (with the reduction of its partials when a.S > 1).

@@ -174,6 +174,34 @@ int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 forward pass (Fast Diffusion Attention, "Results": the FP8 forward).
+ *   q                : [B][T][H][D]    OCP FP8 E4M3 bytes (1 sign, 4 exponent
+ *                      bits with bias 7, 3 mantissa bits; largest value 448)
+ *   k, v             : [B][T][H_kv][D] E4M3 bytes
+ *   q_descale        : [B][H] float32, k_descale and v_descale [B][H_kv]:
+ *                      the value a byte stands for is descale * e4m3(byte)
+ *   out              : [B][T][H][D] bf16;  lse : [B][H][T] fp32 (natural log)
+ * The scores are scale * q_descale * k_descale * (q . k) with the products
+ * of the E4M3 values accumulated in float32.  The softmax runs in float32;
+ * its unnormalised probabilities 2^(s log2(e) - m) (m within 8 of the row
+ * maximum, so at most 2^8) are rounded to E4M3 for the P.V product, and
+ * the denominator sums the unrounded values.  That rounding is the one
+ * approximation beyond the bf16 pass: it moves an output element by at
+ * most 2^-4 sum_j P_ij |v_j| + 2^-10 sum_j |v_j| / l_i (l_i the row sum at
+ * the maximum).  T = 2n (diffusion, block_size as above) or S (causal).
+ * Grouped heads as in the _gqa entry points.  Same pointer, size and
+ * error rules as diffusion_attn_fwd, plus: the descale arrays must be
+ * non-NULL and 4-byte aligned.  There is no FP8 backward.
+ */
+int diffusion_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                           const float* k_descale, const float* v_descale, void* out, float* lse,
+                           int B, int n, int H, int H_kv, int D, int block_size, float scale,
+                           void* stream);
+int causal_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, const float* v_descale, void* out, float* lse,
+                        int B, int S, int H, int H_kv, int D, float scale, void* stream);
+
+/*
  * Packed batches of samples of different lengths (Fast Diffusion
  * Attention, "Hopper": varlen batches, as in supervised fine-tuning).
  *   cu_seqlens : B + 1 int32 token offsets in device memory, 4-byte aligned

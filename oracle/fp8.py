@@ -59,9 +59,11 @@ def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, b: int, scale: floa
     return diffusion_forward(q, k, v, b, scale)
 
 
-def fp8_output_bound(q, k, v, b: int, scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+def fp8_output_bound(q, k, v, b: int, scale: float, rows: Optional[Sequence[int]] = None,
+                     mask: Optional[np.ndarray] = None) -> np.ndarray:
     """Largest error the E4M3 rounding of P~ can cause in O[rows] (float64
-    q, k, v of shape (2n, D), already dequantized).
+    q, k, v of shape (2n, D), already dequantized).  ``mask`` (rows x keys)
+    replaces the block-diffusion mask, e.g. with the causal one.
 
     The kernel rounds P~_ij = 2^(s_ij c - m_i) with a reference m_i at or
     below the row maximum (so P~ <= 2^8 and its row sum l_i' is at least
@@ -71,9 +73,13 @@ def fp8_output_bound(q, k, v, b: int, scale: float, rows: Optional[Sequence[int]
         |dO_id| <= 2^-4 sum_j P_ij |v_jd| + 2^-10 sum_{j visible} |v_jd| / l_i
     with P the exact probabilities and l_i = sum_j exp(s_ij - max_j s_ij).
     """
-    n = _half_len(q)
-    rows = np.arange(2 * n) if rows is None else np.asarray(rows, dtype=np.int64)
-    M = block_diffusion_mask(n, b, rows)
+    if mask is None:
+        n = _half_len(q)
+        rows = np.arange(2 * n) if rows is None else np.asarray(rows, dtype=np.int64)
+        M = block_diffusion_mask(n, b, rows)
+    else:
+        rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+        M = mask
     S = np.where(M, scale * (q[rows] @ k.T), -np.inf)
     E = np.exp(S - S.max(axis=1, keepdims=True))
     ell = E.sum(axis=1)

@@ -231,3 +231,15 @@ def test_one_more_token_past_the_largest_sample_is_rejected():
     assert _fwd(n=16384, H=256, D=128) == UNSUPPORTED
     assert bd.diffusion_attn_bwd_workspace_size(1, 16383, 256, 128) > 0
     assert bd.diffusion_attn_bwd_workspace_size(1, 16384, 256, 128) == 0
+
+
+def test_fp8_forward_rejects_bad_arguments():
+    lib = bd.lib()
+    f = lambda qd=FAKE, kd=FAKE, vd=FAKE, D=64, H_kv=2: lib.diffusion_attn_fwd_fp8(
+        FAKE, FAKE, FAKE, qd, kd, vd, FAKE, FAKE, 1, 16, 4, H_kv, D, 4, 0.125, None)
+    assert f(qd=None) == INVALID and f(kd=None) == INVALID and f(vd=None) == INVALID
+    assert f(vd=FAKE + 2) == INVALID            # descales must be 4-byte aligned
+    assert f(D=96) == UNSUPPORTED
+    assert f(H_kv=3) == INVALID
+    assert lib.causal_attn_fwd_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 4, 64, 0.1,
+                                   None) == INVALID

@@ -26,8 +26,9 @@ import torch
 
 import oracle
 import block_diffusion_lm_amd as bd
-from workloads import (GQA_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, make_causal_view, make_inputs,
-                       make_varlen_inputs, make_varlen_workload_inputs, make_workload_inputs)
+from workloads import (GQA_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, make_causal_view, make_fp8_inputs,
+                       make_fp8_integer_score_inputs, make_inputs, make_varlen_inputs,
+                       make_varlen_workload_inputs, make_workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -705,3 +706,119 @@ def test_largest_accepted_sample():
     dk_ref, dv_ref = oracle.diffusion_grad_kv_cols(qh, kh, vh, dh, Of, Lf, b, scale, cols)
     check_grad(res["dk"][0, cols, hi], dk_ref, "dk", "largest sample")
     check_grad(res["dv"][0, cols, hi], dv_ref, "dv", "largest sample")
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) forward
+# ---------------------------------------------------------------------------
+
+def run_fp8(q8, k8, v8, qd, kd, vd, b, scale, causal=False):
+    dev = _dev()
+    B, T, H, D = q8.shape
+    Hkv = k8.shape[2]
+    q8, k8, v8, qd, kd, vd = (x.to(dev) for x in (q8, k8, v8, qd, kd, vd))
+    out = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if causal:
+        bd.causal_attn_fwd_fp8(q8, k8, v8, qd, kd, vd, out, lse, B, T, H, Hkv, D, scale)
+    else:
+        bd.diffusion_attn_fwd_fp8(q8, k8, v8, qd, kd, vd, out, lse, B, T // 2, H, Hkv, D, b, scale)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _fp8_head(q8, k8, v8, qd, kd, vd, bi, h):
+    """Dequantized float64 q, k, v of (sample bi, query head h)."""
+    G = q8.shape[2] // k8.shape[2]
+    u8 = lambda t, hh: t[bi, :, hh].view(torch.uint8).numpy()
+    return (oracle.dequantize_e4m3(u8(q8, h), float(qd[bi, h])),
+            oracle.dequantize_e4m3(u8(k8, h // G), float(kd[bi, h // G])),
+            oracle.dequantize_e4m3(u8(v8, h // G), float(vd[bi, h // G])))
+
+
+def check_fp8_head(out, lse, q, k, v, b, scale, rows, what, exact_p=False, causal=False):
+    """O and LSE of one head against exact attention on the dequantized
+    values.  exact_p: every probability is exact in E4M3 (integer scores),
+    so the bf16 tolerances apply; otherwise O may also move by the bound of
+    the E4M3 rounding of P."""
+    if causal:
+        O, L = oracle.causal_forward(q, k, v, scale)
+        O, L = O[rows], L[rows]
+    else:
+        O, L = oracle.diffusion_forward_rows(q, k, v, b, scale, rows)
+    o = oracle.to_f64(out)
+    if exact_p:
+        check_fwd(out, lse, O, L, what)
+        return
+    mask = oracle.causal_mask(q.shape[0], rows) if causal else None
+    bound = oracle.fp8_output_bound(q, k, v, b, scale, rows, mask=mask)
+    err = np.abs(o - O)
+    tol = bound + _halfulp_bf16(O) + 1e-3
+    assert np.all(err <= tol), f"{what}: error {err.max():.3g} beyond the E4M3 bound (max {bound.max():.3g})"
+    lerr = np.abs(oracle.to_f64(lse) - L).max()
+    assert lerr <= LSE_TOL, f"{what}: LSE error {lerr:.3g}"
+    print(f"[{what}] fp8 max err {err.max():.3g} (bound up to {bound.max():.3g}), lse err {lerr:.3g}")
+
+
+FP8_SHAPES = [  # B, n, H, H_kv, D, b
+    (1, 128, 2, 2, 64, 4), (2, 129, 3, 3, 128, 16), (1, 300, 4, 2, 128, 7),
+    (2, 64, 4, 1, 64, 200), (1, 7, 2, 2, 128, 3), (1, 257, 2, 1, 64, 1),
+]
+
+
+@pytest.mark.parametrize("B,n,H,Hkv,D,b", FP8_SHAPES)
+def test_fp8_integer_scores_exact(B, n, H, Hkv, D, b):
+    """Scores that are small integers make every probability a power of two,
+    exact in E4M3: the FP8 forward must then meet the bf16 tolerances."""
+    q8, k8, v8, qd, kd, vd = make_fp8_integer_score_inputs(B, n, H, D, seed=9960 + n + D, H_kv=Hkv)
+    scale = math.log(2.0)
+    out, lse = run_fp8(q8, k8, v8, qd, kd, vd, b, scale)
+    rows = np.arange(2 * n)
+    for bi in range(B):
+        for h in range(H):
+            q, k, v = _fp8_head(q8, k8, v8, qd, kd, vd, bi, h)
+            check_fp8_head(out[bi, :, h], lse[bi, h], q, k, v, b, scale, rows,
+                           f"fp8 exact n{n} D{D} ({bi},{h})", exact_p=True)
+
+
+@pytest.mark.parametrize("B,n,H,Hkv,D,b", FP8_SHAPES)
+def test_fp8_random_within_bound(B, n, H, Hkv, D, b):
+    q8, k8, v8, qd, kd, vd = make_fp8_inputs(B, n, H, D, seed=9970 + n + D, H_kv=Hkv)
+    scale = 1 / math.sqrt(D)
+    out, lse = run_fp8(q8, k8, v8, qd, kd, vd, b, scale)
+    rows = np.arange(2 * n)
+    for bi in range(B):
+        for h in range(H):
+            q, k, v = _fp8_head(q8, k8, v8, qd, kd, vd, bi, h)
+            check_fp8_head(out[bi, :, h], lse[bi, h], q, k, v, b, scale, rows, f"fp8 n{n} D{D} ({bi},{h})")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_negative_scale_and_causal(D):
+    q8, k8, v8, qd, kd, vd = make_fp8_inputs(1, 150, 2, D, seed=9980 + D)
+    out, lse = run_fp8(q8, k8, v8, qd, kd, vd, 16, -0.2)
+    for h in range(2):
+        q, k, v = _fp8_head(q8, k8, v8, qd, kd, vd, 0, h)
+        check_fp8_head(out[0, :, h], lse[0, h], q, k, v, 16, -0.2, np.arange(300), f"fp8 scale -0.2 D{D}")
+    S = 150
+    cq, ck, cv = (x[:, :S].contiguous() for x in (q8, k8, v8))
+    out, lse = run_fp8(cq, ck, cv, qd, kd, vd, 1, 1 / math.sqrt(D), causal=True)
+    for h in range(2):
+        q, k, v = _fp8_head(cq, ck, cv, qd, kd, vd, 0, h)
+        check_fp8_head(out[0, :, h], lse[0, h], q, k, v, 1, 1 / math.sqrt(D), np.arange(S),
+                       f"fp8 causal D{D}", causal=True)
+
+
+def test_fp8_long_sequence_sampled():
+    """The long-sequence shape (B=2, n=8192, H=32, D=128, b=32) in FP8: all
+    rows of two heads."""
+    B, n, H, D, b = 2, 8192, 32, 128, 32
+    q8, k8, v8, qd, kd, vd = make_fp8_inputs(B, n, H, D, seed=9990)
+    scale = 1 / math.sqrt(D)
+    out, lse = run_fp8(q8, k8, v8, qd, kd, vd, b, scale)
+    for bi, h in ((0, 0), (1, 31)):
+        q, k, v = _fp8_head(q8, k8, v8, qd, kd, vd, bi, h)
+        for r0 in range(0, 2 * n, 4096):
+            rows = np.arange(r0, r0 + 4096)
+            check_fp8_head(out[bi, rows, h], lse[bi, h, rows], q, k, v, b, scale, rows,
+                           f"fp8 long ({bi},{h}) rows {r0}..")

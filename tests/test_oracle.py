@@ -639,3 +639,21 @@ def test_fp8_output_bound_needs_its_subnormal_term():
     P /= P.sum()
     assert err <= bound
     assert err > 2.0 ** -4 * (P @ np.abs(v))[0, 0]
+
+
+def test_fp8_output_bound_with_an_explicit_mask():
+    """Passing the block-diffusion mask explicitly gives the default bound;
+    the causal mask bounds the causal pass."""
+    n, D, b, scale = 30, 8, 4, 0.5
+    q, k, v = (_rand((2 * n, D), s) for s in (90, 91, 92))
+    rows = [0, 5, n, 2 * n - 1]
+    np.testing.assert_array_equal(
+        oracle.fp8_output_bound(q, k, v, b, scale, rows),
+        oracle.fp8_output_bound(q, k, v, b, scale, rows, mask=oracle.block_diffusion_mask(n, b, rows)))
+    O, _ = oracle.causal_forward(q, k, v, scale)
+    # P rounded as the kernel would, with the row maximum as reference
+    s2 = np.where(oracle.causal_mask(2 * n), scale * (q @ k.T) * math.log2(math.e), -np.inf)
+    pt = np.exp2(s2 - s2.max(axis=1, keepdims=True))
+    p8 = torch.from_numpy(pt).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    err = np.abs((p8 @ v) / pt.sum(axis=1, keepdims=True) - O)
+    assert np.all(err <= oracle.fp8_output_bound(q, k, v, 1, scale, mask=oracle.causal_mask(2 * n)))
