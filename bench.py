@@ -507,7 +507,7 @@ def main():
     from block_diffusion_lm_amd import profiling
     traffic = None
     tr = profiling.read_traffic(os.path.join(args.profiles, f"traffic_{dom}_{w.name}.txt"))
-    if tr and tr.get("source_sha256") == profiling.source_hash():
+    if tr and tr.get("source_sha256") == profiling.source_hash(dom):
         traffic = float(tr["bytes_per_launch"])
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,

@@ -14,9 +14,9 @@ writes two short text files:
   dominant (longest) kernel from two ``--pmc`` runs (FETCH_SIZE, then
   WRITE_SIZE, KiB per dispatch).  Each counter is scaled by what it reads
   for the device copy of known size that the same run performs
-  (``bench.py --copy-calibration-mib``).  The file records a hash of the
-  kernel sources; ``bench.py`` reports the figure only while the sources
-  still hash the same.
+  (``bench.py --copy-calibration-mib``).  The file records a hash of that
+  kernel's sources (the shared headers and its own file); ``bench.py``
+  reports the figure only while they still hash the same.
 """
 from __future__ import annotations
 
@@ -37,14 +37,23 @@ KERNELS = {
 COPY_SYMBOL = "copyBuffer"
 
 
-def source_hash() -> str:
-    """sha256 over the kernel sources (file names and contents)."""
+# the source file that holds each timed kernel
+KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "bwd_dq": "attn_bwd.hip", "bwd_dkdv": "attn_bwd.hip",
+                  "fwd_fp8": "attn_fwd_fp8.hip"}
+
+
+def source_hash(kernel: Optional[str] = None) -> str:
+    """sha256 over kernel sources (file names and contents): the shared
+    headers plus the file holding ``kernel``, or every source when None."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+        if not name.endswith((".h", ".hip", ".cpp")):
+            continue
+        if kernel is not None and not name.endswith(".h") and name != KERNEL_SOURCES[kernel]:
+            continue
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -101,7 +110,7 @@ def summarize(workload: str, trace: str, fetch: Optional[str], write: Optional[s
     stats = kernel_stats(trace)
     ours = {n: s for n, s in stats.items() if "bd::" in n}
     lines = [f"# rocprofv3 kernel trace, workload {workload}", f"# command: {command}",
-             f"# kernel sources sha256: {source_hash()}", "",
+             f"# kernel sources sha256 (all files): {source_hash()}", "",
              f"{'kernel':58s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s}"]
     for name, s in sorted(ours.items(), key=lambda kv: -kv[1]["avg_ns"]):
         lines.append(f"{name.replace('void ', '')[:58]:58s} {s['calls']:6d} {s['avg_ns'] / 1e3:10.1f} "
@@ -131,7 +140,7 @@ def summarize(workload: str, trace: str, fetch: Optional[str], write: Optional[s
         f"kernel: {dom}",
         f"kernel_symbol: {dom_name}",
         f"workload: {workload}",
-        f"source_sha256: {source_hash()}",
+        f"source_sha256: {source_hash(dom)}",
         f"fetch_kib_per_dispatch: {f_k:.1f}",
         f"write_kib_per_dispatch: {w_k:.1f}",
         f"copy_fetch_kib: {f_copy:.1f}",
