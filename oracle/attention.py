@@ -32,6 +32,11 @@ Readings where the pages are silent (each listed in the design notes):
 * The log-sum-exp is the natural logarithm and includes the scale.
 * The causal yardstick is top-left causal: row i of a sequence sees keys
   0..i of the same sequence.
+* Softcapping (named by Fast Diffusion Attention, "Accuracy", among what
+  its tests cover; defined by flash-attention, whose interface the pages
+  follow): with cap > 0 the scaled scores s become cap * tanh(s / cap)
+  before the softmax; the backward multiplies dS by 1 - tanh^2(s / cap)
+  (the derivative of that map).  cap = 0 leaves the scores as they are.
 """
 from __future__ import annotations
 
@@ -94,25 +99,37 @@ def _masked_softmax_stats(S: np.ndarray, M: np.ndarray):
     return P, lse
 
 
+def _scores(q, k, scale, softcap):
+    """Scaled scores, softcapped when softcap > 0; also returns the factor
+    d(capped)/d(scaled) = 1 - tanh^2 (None without softcap)."""
+    S = scale * (q @ k.T)
+    if not softcap:
+        return S, None
+    T = np.tanh(S / softcap)
+    return softcap * T, 1.0 - T * T
+
+
 def masked_attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-                             M: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                             M: np.ndarray, scale: float, softcap: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
     """O = softmax(scale * q k^T restricted to M) v and its row log-sum-exp.
 
     q: (Nq, D), k and v: (Nk, D), M: (Nq, Nk) boolean.  float64 throughout.
     """
-    S = scale * (q @ k.T)
+    S, _ = _scores(q, k, scale, softcap)
     P, lse = _masked_softmax_stats(S, M)
     return P @ v, lse
 
 
-def masked_attention_backward(q, k, v, dout, M, scale):
+def masked_attention_backward(q, k, v, dout, M, scale, softcap: float = 0.0):
     """Analytic gradients (dq, dk, dv) of sum(dout * O) for masked attention."""
-    S = scale * (q @ k.T)
+    S, dcap = _scores(q, k, scale, softcap)
     P, _ = _masked_softmax_stats(S, M)
     dv = P.T @ dout
     dP = dout @ v.T
     delta = (P * dP).sum(axis=1)
     dS = P * (dP - delta[:, None])
+    if dcap is not None:
+        dS = dS * dcap
     dq = scale * (dS @ k)
     dk = scale * (dS.T @ q)
     return dq, dk, dv
@@ -128,41 +145,44 @@ def _half_len(x: np.ndarray) -> int:
     return x.shape[0] // 2
 
 
-def diffusion_forward(q, k, v, b: int, scale: float):
+def diffusion_forward(q, k, v, b: int, scale: float, softcap: float = 0.0):
     """(O, LSE) of one head: O (2n, D), LSE (2n,), natural log."""
     n = _half_len(q)
-    return masked_attention_forward(q, k, v, block_diffusion_mask(n, b), scale)
+    return masked_attention_forward(q, k, v, block_diffusion_mask(n, b), scale, softcap)
 
 
-def diffusion_backward(q, k, v, dout, b: int, scale: float):
+def diffusion_backward(q, k, v, dout, b: int, scale: float, softcap: float = 0.0):
     """(dq, dk, dv) of one head."""
     n = _half_len(q)
-    return masked_attention_backward(q, k, v, dout, block_diffusion_mask(n, b), scale)
+    return masked_attention_backward(q, k, v, dout, block_diffusion_mask(n, b), scale, softcap)
 
 
-def diffusion_forward_rows(q, k, v, b: int, scale: float, rows: Sequence[int]):
+def diffusion_forward_rows(q, k, v, b: int, scale: float, rows: Sequence[int], softcap: float = 0.0):
     """O and LSE of the query rows ``rows`` only (same definition, fewer rows)."""
     n = _half_len(q)
     rows = np.asarray(rows, dtype=np.int64)
     M = block_diffusion_mask(n, b, rows)
-    return masked_attention_forward(q[rows], k, v, M, scale)
+    return masked_attention_forward(q[rows], k, v, M, scale, softcap)
 
 
-def diffusion_grad_q_rows(q, k, v, dout, b: int, scale: float, rows: Sequence[int]):
+def diffusion_grad_q_rows(q, k, v, dout, b: int, scale: float, rows: Sequence[int],
+                          softcap: float = 0.0):
     """dQ of the query rows ``rows``: each row needs only its own softmax."""
     n = _half_len(q)
     rows = np.asarray(rows, dtype=np.int64)
     M = block_diffusion_mask(n, b, rows)
-    S = scale * (q[rows] @ k.T)
+    S, dcap = _scores(q[rows], k, scale, softcap)
     P, _ = _masked_softmax_stats(S, M)
     dP = dout[rows] @ v.T
     delta = (P * dP).sum(axis=1)
     dS = P * (dP - delta[:, None])
+    if dcap is not None:
+        dS = dS * dcap
     return scale * (dS @ k)
 
 
 def diffusion_grad_kv_cols(q, k, v, dout, out, lse, b: int, scale: float,
-                           cols: Sequence[int]):
+                           cols: Sequence[int], softcap: float = 0.0):
     """dK and dV of the key columns ``cols``.
 
     A key's gradient sums over every query that sees it, so it needs each
@@ -175,11 +195,13 @@ def diffusion_grad_kv_cols(q, k, v, dout, out, lse, b: int, scale: float,
     n = _half_len(q)
     cols = np.asarray(cols, dtype=np.int64)
     M = block_diffusion_mask(n, b)[:, cols]
-    S = scale * (q @ k[cols].T)
+    S, dcap = _scores(q, k[cols], scale, softcap)
     P = np.where(M, np.exp(np.where(M, S, 0.0) - lse[:, None]), 0.0)
     dP = dout @ v[cols].T
     delta = (dout * out).sum(axis=1)
     dS = P * (dP - delta[:, None])
+    if dcap is not None:
+        dS = dS * dcap
     dv = P.T @ dout
     dk = scale * (dS.T @ q)
     return dk, dv
@@ -189,12 +211,12 @@ def diffusion_grad_kv_cols(q, k, v, dout, out, lse, b: int, scale: float,
 # Causal yardstick of one sequence: q, k, v of shape (S, D)
 # --------------------------------------------------------------------------
 
-def causal_forward(q, k, v, scale: float):
-    return masked_attention_forward(q, k, v, causal_mask(q.shape[0]), scale)
+def causal_forward(q, k, v, scale: float, softcap: float = 0.0):
+    return masked_attention_forward(q, k, v, causal_mask(q.shape[0]), scale, softcap)
 
 
-def causal_backward(q, k, v, dout, scale: float):
-    return masked_attention_backward(q, k, v, dout, causal_mask(q.shape[0]), scale)
+def causal_backward(q, k, v, dout, scale: float, softcap: float = 0.0):
+    return masked_attention_backward(q, k, v, dout, causal_mask(q.shape[0]), scale, softcap)
 
 
 # --------------------------------------------------------------------------

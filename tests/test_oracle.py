@@ -657,3 +657,82 @@ def test_fp8_output_bound_with_an_explicit_mask():
     p8 = torch.from_numpy(pt).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     err = np.abs((p8 @ v) / pt.sum(axis=1, keepdims=True) - O)
     assert np.all(err <= oracle.fp8_output_bound(q, k, v, 1, scale, mask=oracle.causal_mask(2 * n)))
+
+
+# --------------------------------------------------------------------------
+# Softcapping: scores s -> cap * tanh(s / cap)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,b", [(4, 1), (6, 3), (5, 2)])
+def test_softcap_gradients_match_central_differences(n, b):
+    D, scale, cap, eps = 4, 0.9, 1.5, 1e-6
+    q, k, v, do = (3.0 * _rand((2 * n, D), s) for s in (100, 101, 102, 103))
+    dq, dk, dv = oracle.diffusion_backward(q, k, v, do, b, scale, softcap=cap)
+
+    def loss(qq, kk, vv):
+        return float((oracle.diffusion_forward(qq, kk, vv, b, scale, softcap=cap)[0] * do).sum())
+
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        err = np.abs(num - grad).max() / np.abs(grad).max()
+        assert err <= 1e-6, (which, err)
+
+
+def test_softcap_limits_and_bounds():
+    """A very large cap is no cap; the capped scores lie in (-cap, cap), so
+    within a row no probability exceeds another by more than e^(2 cap),
+    however large the raw scores; q = 0 still gives uniform rows."""
+    n, b, D, scale = 12, 4, 6, 0.7
+    q, k, v, do = (_rand((2 * n, D), s) for s in (104, 105, 106, 107))
+    O, L = oracle.diffusion_forward(q, k, v, b, scale)
+    Oc, Lc = oracle.diffusion_forward(q, k, v, b, scale, softcap=1e7)
+    np.testing.assert_allclose(Oc, O, atol=1e-9)
+    np.testing.assert_allclose(Lc, L, atol=1e-9)
+    for x, y in zip(oracle.diffusion_backward(q, k, v, do, b, scale, softcap=1e7),
+                    oracle.diffusion_backward(q, k, v, do, b, scale)):
+        np.testing.assert_allclose(x, y, atol=1e-9)
+    cap = 2.0
+    big_q = 50.0 * q
+    M = oracle.block_diffusion_mask(n, b)
+    onehot = np.eye(2 * n)[:, :2 * n]
+    P, _ = oracle.diffusion_forward(big_q, k, onehot, b, scale, softcap=cap)  # O = P when v = I
+    for r in range(2 * n):
+        pr = P[r][M[r]]
+        assert pr.max() / pr.min() <= math.exp(2 * cap) * (1 + 1e-9)
+    Oz, _ = oracle.diffusion_forward(np.zeros_like(q), k, v, b, scale, softcap=cap)
+    Ou, _ = oracle.diffusion_forward(np.zeros_like(q), k, v, b, scale)
+    np.testing.assert_allclose(Oz, Ou, atol=1e-13)
+
+
+def test_softcap_two_key_row_by_hand():
+    """A clean row of the first block with b = 2 sees exactly two keys; its
+    output is their average weighted by exp(cap tanh(s / cap))."""
+    n, b, D, scale, cap = 4, 2, 3, 0.5, 0.8
+    q, k, v = (_rand((2 * n, D), s) for s in (108, 109, 110))
+    O, L = oracle.diffusion_forward(q, k, v, b, scale, softcap=cap)
+    r = n + 1                         # clean row 1 sees clean keys 0 and 1
+    s = [scale * float(q[r] @ k[n + j]) for j in (0, 1)]
+    w = [math.exp(cap * math.tanh(x / cap)) for x in s]
+    np.testing.assert_allclose(O[r], (w[0] * v[n] + w[1] * v[n + 1]) / (w[0] + w[1]), atol=1e-14)
+    assert abs(L[r] - math.log(w[0] + w[1])) < 1e-14
+
+
+def test_softcap_sampled_forms_equal_full():
+    n, b, D, scale, cap = 20, 3, 8, 0.4, 1.2
+    q, k, v, do = (2.0 * _rand((2 * n, D), s) for s in (111, 112, 113, 114))
+    O, lse = oracle.diffusion_forward(q, k, v, b, scale, softcap=cap)
+    dq, dk, dv = oracle.diffusion_backward(q, k, v, do, b, scale, softcap=cap)
+    rows = [0, 4, n - 1, n, n + 9, 2 * n - 1]
+    Or, lr = oracle.diffusion_forward_rows(q, k, v, b, scale, rows, softcap=cap)
+    np.testing.assert_allclose(Or, O[rows], atol=1e-13)
+    np.testing.assert_allclose(oracle.diffusion_grad_q_rows(q, k, v, do, b, scale, rows, softcap=cap),
+                               dq[rows], atol=1e-12)
+    dkc, dvc = oracle.diffusion_grad_kv_cols(q, k, v, do, O, lse, b, scale, rows, softcap=cap)
+    np.testing.assert_allclose(dkc, dk[rows], atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[rows], atol=1e-12)
