@@ -223,7 +223,7 @@ def setup_batched(w, dev, torch, bd):
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, Hkv, D, b,
-                                scale, ws, ws_bytes)
+                                scale, 0.0, ws, ws_bytes)
             mark(ev, 2 + stage)
 
     def causal_step(ev=None):
@@ -235,7 +235,7 @@ def setup_batched(w, dev, torch, bd):
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, None, 2 * B, n, 0,
-                                H, Hkv, D, 1, scale, cws)
+                                H, Hkv, D, 1, scale, 0.0, cws)
             mark(ev, 2 + stage)
 
     def ungrouped():
@@ -254,7 +254,7 @@ def setup_batched(w, dev, torch, bd):
                 for _ in range(reps):
                     for stage in range(2):
                         bd.bdattn_bwd_stage(MD, stage, q, kk, vv, out, do, lse, dq, gk, gv, None, B, n, 0, H,
-                                            hk, D, b, scale, ws, ws_bytes)
+                                            hk, D, b, scale, 0.0, ws, ws_bytes)
                 e1.record()
                 torch.cuda.synchronize()
                 times[name].append(e0.elapsed_time(e1) / reps)
@@ -313,7 +313,7 @@ def setup_varlen(w, dev, torch, bd):
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, cu_t, B, max_n, total, H, Hkv,
-                                D, b, scale, ws, ws_bytes)
+                                D, b, scale, 0.0, ws, ws_bytes)
             mark(ev, 2 + stage)
 
     def causal_step(ev=None):
@@ -322,7 +322,7 @@ def setup_varlen(w, dev, torch, bd):
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MC, stage, q, k, v, cout, do, clse, cdq, cdk, cdv, ccu_t, 2 * B, max_n, total,
-                                H, Hkv, D, 1, scale, cws, cws_bytes)
+                                H, Hkv, D, 1, scale, 0.0, cws, cws_bytes)
             mark(ev, 2 + stage)
 
     def cpu_heads():

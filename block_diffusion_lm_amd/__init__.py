@@ -11,7 +11,10 @@ from ._binding import (  # noqa: F401
     MODE_DIFFUSION,
     NOISY,
     SIGNATURES,
+    bdattn_bwd,
     bdattn_bwd_stage,
+    bdattn_bwd_workspace_size,
+    bdattn_fwd,
     bdattn_bwd_tiles,
     bdattn_fwd_tiles,
     bdattn_row_interval,

@@ -31,7 +31,10 @@ SIGNATURES = {
     "causal_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
-    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 10 + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "bdattn_bwd_stage": (_i, [_i, _i] + [_vp] * 10 + [_i] * 7 + [_f, _f, _vp, _sz, _vp]),
+    "bdattn_fwd": (_i, [_i] + [_vp] * 6 + [_i] * 7 + [_f, _f, _vp]),
+    "bdattn_bwd_workspace_size": (_sz, [_i] * 8),
+    "bdattn_bwd": (_i, [_i] + [_vp] * 10 + [_i] * 7 + [_f, _f, _vp, _sz, _vp]),
     "diffusion_attn_fwd_fp8": (_i, [_vp] * 8 + [_i] * 6 + [_f, _vp]),
     "causal_attn_fwd_fp8": (_i, [_vp] * 8 + [_i] * 5 + [_f, _vp]),
     "diffusion_attn_varlen_fwd": (_i, [_vp] * 6 + [_i] * 7 + [_f, _vp]),
@@ -183,8 +186,8 @@ def _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, T, H, H_kv, D, workspace, 
 
 
 def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, n,
-                     total_tokens, H, H_kv, D, block_size, scale, workspace, workspace_bytes=None,
-                     stream=None):
+                     total_tokens, H, H_kv, D, block_size, scale, softcap, workspace,
+                     workspace_bytes=None, stream=None):
     """One backward stage (0: dQ, also writing -delta and lse2; 1: dK/dV).
 
     cu_seqlens None: batched tensors, n the half length (S in causal mode),
@@ -201,9 +204,49 @@ def bdattn_bwd_stage(mode, stage, q, k, v, out, dout, lse, dq, dk, dv, cu_seqlen
         cu = _ptr(cu_seqlens)
     _check(lib().bdattn_bwd_stage(mode, stage, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                                   _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), cu, B, n, total_tokens,
-                                  H, H_kv, D, block_size, float(scale), _ptr(workspace), wsb,
-                                  _stream_handle(q, stream)),
+                                  H, H_kv, D, block_size, float(scale), float(softcap),
+                                  _ptr(workspace), wsb, _stream_handle(q, stream)),
            "bdattn_bwd_stage")
+
+
+# The general form: mode, batched (cu_seqlens None) or packed tensors, grouped
+# heads and softcapping (0: off) in one call.
+
+def _general_checks_fwd(mode, q, k, v, out, lse, cu_seqlens, B, n, total_tokens, H, H_kv, D):
+    if cu_seqlens is None:
+        _want_fwd(q, k, v, out, lse, B, 2 * n if mode == MODE_DIFFUSION else n, H, H_kv, D)
+        return None
+    _want_fwd_packed(q, k, v, out, lse, cu_seqlens, B, total_tokens, H, H_kv, D)
+    return _ptr(cu_seqlens)
+
+
+def bdattn_fwd(mode, q, k, v, out, lse, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size, scale,
+               softcap=0.0, stream=None):
+    cu = _general_checks_fwd(mode, q, k, v, out, lse, cu_seqlens, B, n, total_tokens, H, H_kv, D)
+    _check(lib().bdattn_fwd(mode, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), cu, B, n, total_tokens,
+                            H, H_kv, D, block_size, float(scale), float(softcap), _stream_handle(q, stream)),
+           "bdattn_fwd")
+
+
+def bdattn_bwd_workspace_size(mode, packed, B, n, total_tokens, H, H_kv, D) -> int:
+    return int(lib().bdattn_bwd_workspace_size(mode, int(bool(packed)), B, n, total_tokens, H, H_kv, D))
+
+
+def bdattn_bwd(mode, q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, n, total_tokens, H, H_kv, D,
+               block_size, scale, softcap, workspace, workspace_bytes=None, stream=None):
+    if cu_seqlens is None:
+        wsb = _want_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, 2 * n if mode == MODE_DIFFUSION else n,
+                        H, H_kv, D, workspace, workspace_bytes)
+        cu = None
+    else:
+        wsb = _want_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens, B, total_tokens, H,
+                               H_kv, D, workspace, workspace_bytes)
+        cu = _ptr(cu_seqlens)
+    _check(lib().bdattn_bwd(mode, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), cu, B, n, total_tokens, H, H_kv, D, block_size,
+                            float(scale), float(softcap), _ptr(workspace), wsb,
+                            _stream_handle(q, stream)),
+           "bdattn_bwd")
 
 
 # Packed samples of different lengths: q / out / dout / dq [total][H][D],

@@ -26,6 +26,7 @@ struct Problem {
   float scale;
   const int32_t* cu;  // packed only
   int total;          // packed only
+  float softcap;      // > 0: scores capped to softcap * tanh(s / softcap); 0: off
   bool packed() const { return cu != nullptr; }
   int T() const { return mode == bd::MODE_CAUSAL ? n : 2 * n; }
   long long tokens() const { return packed() ? (long long)total : (long long)B * T(); }
@@ -51,6 +52,7 @@ int check_problem(const Problem& p) {
   if (p.tokens() * p.H > (long long)std::numeric_limits<int>::max()) return BDATTN_ERR_INVALID;
   if (T * p.H * p.D * 2 >= (1LL << 31)) return BDATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(p.scale) || p.scale == 0.f) return BDATTN_ERR_INVALID;
+  if (!std::isfinite(p.softcap) || p.softcap < 0.f) return BDATTN_ERR_INVALID;
   return BDATTN_OK;
 }
 
@@ -89,6 +91,7 @@ bd::AttnArgs make_args(const Problem& p) {
   a.nhalves = (p.mode == bd::MODE_CAUSAL) ? 1 : 2;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.softcap = p.softcap;
   a.cu = p.cu;
   a.tokens = p.tokens();
   a.stat_hs = p.packed() ? p.total : p.T();
@@ -166,12 +169,21 @@ int run_bwd(const Problem& p, int stage, const void* q, const void* k, const voi
 }
 
 Problem batched(int mode, int B, int n, int H, int H_kv, int D, int b, float scale) {
-  return Problem{mode, B, n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, nullptr, 0};
+  return Problem{mode, B, n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, nullptr, 0, 0.f};
 }
 
 Problem packed(int mode, const int32_t* cu, int B, int max_n, int total, int H, int H_kv, int D,
                int b, float scale) {
-  return Problem{mode, B, max_n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, cu, total};
+  return Problem{mode, B, max_n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, cu, total, 0.f};
+}
+
+// The general form: batched (cu NULL) or packed, either mode, with softcap.
+Problem general(int mode, const int32_t* cu, int B, int n, int total, int H, int H_kv, int D, int b,
+                float scale, float softcap) {
+  Problem p = cu ? packed(mode, cu, B, n, total, H, H_kv, D, b, scale)
+                 : batched(mode, B, n, H, H_kv, D, b, scale);
+  p.softcap = softcap;
+  return p;
 }
 
 bool geom_args_ok(int mode, int n, int b) {
@@ -346,19 +358,48 @@ int causal_attn_varlen_bwd(const void* q, const void* k, const void* v, const vo
                  -1, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
+// ---- the general form ----------------------------------------------------------
+
+int bdattn_fwd(int mode, const void* q, const void* k, const void* v, void* out, float* lse,
+               const int32_t* cu_seqlens, int B, int n, int total_tokens, int H, int H_kv, int D,
+               int block_size, float scale, float softcap, void* stream) {
+  if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
+  if (cu_seqlens && total_tokens == 0) return BDATTN_OK;
+  return run_fwd(general(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size, scale, softcap),
+                 q, k, v, out, lse, stream);
+}
+
+size_t bdattn_bwd_workspace_size(int mode, int packed_, int B, int n, int total_tokens, int H,
+                                 int H_kv, int D) {
+  if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return 0;
+  if (packed_ && total_tokens == 0) return 0;
+  static const int32_t stand_in = 0;  // the offsets are not read here
+  return workspace_bytes(general(mode, packed_ ? &stand_in : nullptr, B, n, total_tokens, H, H_kv, D,
+                                 1, 1.f, 0.f));
+}
+
+int bdattn_bwd(int mode, const void* q, const void* k, const void* v, const void* out,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               const int32_t* cu_seqlens, int B, int n, int total_tokens, int H, int H_kv, int D,
+               int block_size, float scale, float softcap, void* workspace,
+               size_t workspace_bytes_, void* stream) {
+  if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
+  if (cu_seqlens && total_tokens == 0) return BDATTN_OK;
+  return run_bwd(general(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size, scale, softcap),
+                 -1, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
 // ---- one backward stage -----------------------------------------------------
 
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, const int32_t* cu_seqlens, int B, int n, int total_tokens, int H,
-                     int H_kv, int D, int block_size, float scale, void* workspace,
+                     int H_kv, int D, int block_size, float scale, float softcap, void* workspace,
                      size_t workspace_bytes_, void* stream) {
   if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
   if (stage < 0 || stage > 1) return BDATTN_ERR_INVALID;
-  const Problem p = cu_seqlens ? packed(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size,
-                                        scale)
-                               : batched(mode, B, n, H, H_kv, D, block_size, scale);
-  return run_bwd(p, stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+  return run_bwd(general(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size, scale, softcap),
+                 stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
 }
 
 static int list_tiles(bool fwd, int mode, int n, int block_size, int tile_m, int tile_n, int half,

@@ -115,8 +115,10 @@ struct DkdvCfg {
 
 // GROUPED: G > 1 query heads per key/value head (the walk spans several
 // query heads, and with S > 1 the workgroup writes float32 partials); the
-// plain multi-head instance compiles none of that.
-template <int D, bool GROUPED>
+// plain multi-head instance compiles none of that.  SC: softcapping on (the
+// P-wave recomputes P from the capped scores and publishes
+// P (1 - tanh^2), so that the dS-wave's dS carries the cap's derivative).
+template <int D, bool GROUPED, bool SC>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
   using C = DkdvCfg<D>;
   using Tile = typename C::Tile;
@@ -350,13 +352,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
             constexpr int qb = decltype(qbc)::value;
             if (!act[qb]) return;
             floatx16& x = t[qb];
+            floatx16 dc;  // softcapping: 1 - tanh^2 of each score
+            if constexpr (SC) {
+              const Softcap capc = softcap_consts(a.scale, a.softcap);
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
-              x[4 * gq + 0] = fast_exp2(__builtin_fmaf(x[4 * gq + 0], a.scale_log2, -l4.x));
-              x[4 * gq + 1] = fast_exp2(__builtin_fmaf(x[4 * gq + 1], a.scale_log2, -l4.y));
-              x[4 * gq + 2] = fast_exp2(__builtin_fmaf(x[4 * gq + 2], a.scale_log2, -l4.z));
-              x[4 * gq + 3] = fast_exp2(__builtin_fmaf(x[4 * gq + 3], a.scale_log2, -l4.w));
+              for (int gq = 0; gq < 4; ++gq) {
+                const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const float rr = softcap_r(capc, x[4 * gq + u]);
+                  x[4 * gq + u] = fast_exp2(softcap_y(capc, rr) - lv[u]);
+                  dc[4 * gq + u] = 4.f * rr * (1.f - rr);
+                }
+              }
+            } else {
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const float4 l4 = *reinterpret_cast<const float4*>(Ls + 32 * qb + 8 * gq + 4 * h2);
+                x[4 * gq + 0] = fast_exp2(__builtin_fmaf(x[4 * gq + 0], a.scale_log2, -l4.x));
+                x[4 * gq + 1] = fast_exp2(__builtin_fmaf(x[4 * gq + 1], a.scale_log2, -l4.y));
+                x[4 * gq + 2] = fast_exp2(__builtin_fmaf(x[4 * gq + 2], a.scale_log2, -l4.z));
+                x[4 * gq + 3] = fast_exp2(__builtin_fmaf(x[4 * gq + 3], a.scale_log2, -l4.w));
+              }
             }
             if (!full[qb]) {
               // zero the rows that do not see this lane's key: register r
@@ -370,8 +388,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
               }
             }
             const bf16x8 bop[2] = {pack_bf16x8(x, 0), pack_bf16x8(x, 8)};
-            px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, bop[0]);
-            px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, bop[1]);
+            if constexpr (SC) {
+              floatx16 xd;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) xd[r] = x[r] * dc[r];
+              px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, pack_bf16x8(xd, 0));
+              px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, pack_bf16x8(xd, 8));
+            } else {
+              px[(qb * 2 + 0) * 64] = __builtin_bit_cast(u32x4, bop[0]);
+              px[(qb * 2 + 1) * 64] = __builtin_bit_cast(u32x4, bop[1]);
+            }
             product2(Tb, qbc, bop);
           };
           step(Q0{});
@@ -518,7 +544,8 @@ struct DqCfg {
   static constexpr int BUF = 2 * Tile::ELEMS;  // K then V
 };
 
-template <int D>
+// SC: softcapping on (P from the capped scores, dS times 1 - tanh^2).
+template <int D, bool SC>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) {
   using C = DqCfg<D>;
   using Tile = typename C::Tile;
@@ -685,8 +712,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           __builtin_amdgcn_sched_barrier(0);
         }
         // P^T = exp2(S^T * scale * log2 e - LSE * log2 e), dS^T = P^T (dP^T - delta)
+        if constexpr (SC) {
+          // sp becomes P (1 - tanh^2): all that dS needs
+          const Softcap capc = softcap_consts(a.scale, a.softcap);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sp[r] = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
+          for (int r = 0; r < 16; ++r) {
+            const float rr = softcap_r(capc, sp[r]);
+            sp[r] = fast_exp2(softcap_y(capc, rr) - lse2) * (4.f * rr * (1.f - rr));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sp[r] = fast_exp2(__builtin_fmaf(sp[r], a.scale_log2, -lse2));
+        }
         if (!full) {
           // register r holds key c0 + 8 (r / 4) + 4 h2 + r % 4
           const int rl = lo - c0 - 4 * h2, rh = hi - c0 - 4 * h2;
@@ -739,15 +776,26 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     using QC = DqCfg<D>;
     const int qtiles = (a.n + QC::BM - 1) / QC::BM;
     const long long qblocks = (long long)qtiles * a.nhalves * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)qblocks), dim3(QC::NT), 0, s, a, qtiles);
+    if (a.softcap > 0.f)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)qblocks), dim3(QC::NT), 0, s, a, qtiles);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)qblocks), dim3(QC::NT), 0, s, a, qtiles);
   } else {
     using KC = DkdvCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
     const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.Hkv * a.S;
-    if (a.G > 1)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)kblocks), dim3(KC::NT), 0, s, a, ktiles);
+    const dim3 grid((unsigned)kblocks), block(KC::NT);
+    if (a.softcap > 0.f) {
+      if (a.G > 1)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), grid, block, 0, s, a, ktiles);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), grid, block, 0, s, a, ktiles);
+    } else {
+      if (a.G > 1)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), grid, block, 0, s, a, ktiles);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), grid, block, 0, s, a, ktiles);
+    }
     if (a.S > 1) {
       const long long E = a.tokens * a.Hkv * D;
       const long long rblocks = (2 * E / 8 + 255) / 256;

@@ -57,7 +57,9 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
   return (a.mode == MODE_DIFFUSION && half == CLEAN) ? n : 0;
 }
 
-template <int D, int BN, int NW, int NBUF>
+// SC: softcapping on (the scores are capped before the mask and the
+// maximum, and kept in base-2 units).
+template <int D, int BN, int NW, int NBUF, bool SC>
 __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
@@ -120,7 +122,11 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) settle(qf[s]);
   }
-  const float cs = fabsf(a.scale) * kLog2e;
+  // Without softcapping the raw scores are scaled by cs when used; with it
+  // they are first turned into capped base-2 scores (factor 1 afterwards).
+  // Q carries the sign of the scale, so the raw scores are scaled by |scale|.
+  const Softcap capc = SC ? softcap_consts(fabsf(a.scale), a.softcap) : Softcap{0.f, 0.f};
+  const float cs = SC ? 1.f : fabsf(a.scale) * kLog2e;
 
   const Segments seg = fwd_segments(g, a.mode, qh, qt, C::BM, BN);
   const int n0 = seg.count > 0 ? seg.end0 - seg.begin0 : 0;
@@ -204,6 +210,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArg
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_vec_at(Ks + 32 * kb * D + koff[s]), qf[s], acc);
         mfma_burst_end();
+        if constexpr (SC) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = softcap_y(capc, softcap_r(capc, acc[r]));
+        }
         if (cls[kb] == TILE_PARTIAL) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -291,7 +301,10 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   const int qtiles = (a.n + C::BM - 1) / C::BM;
   const long long blocks = (long long)qtiles * a.nhalves * a.B * a.H;
-  hipLaunchKernelGGL((fwd_kernel<D, BN, NW, NBUF>), dim3((unsigned)blocks), dim3(C::NT), 0, s, a, qtiles);
+  if (a.softcap > 0.f)
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, NBUF, true>), dim3((unsigned)blocks), dim3(C::NT), 0, s, a, qtiles);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, NBUF, false>), dim3((unsigned)blocks), dim3(C::NT), 0, s, a, qtiles);
   return hipGetLastError();
 }
 

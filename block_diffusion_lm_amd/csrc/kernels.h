@@ -49,6 +49,7 @@ struct AttnArgs {
   int nhalves;  // 2 or 1
   float scale;       // multiplies q.k (may be negative)
   float scale_log2;  // scale * log2(e)
+  float softcap;     // > 0: scaled scores s become softcap * tanh(s / softcap); 0: off
 };
 
 // Query-stationary grids enumerate (sample, query head) pairs as
@@ -94,6 +95,23 @@ __device__ __forceinline__ bool sample_of(const AttnArgs& a, int bi, size_t& tok
   tok0 = stat0 = (size_t)(c0 < 0 ? 0 : c0);
   return c0 >= 0 && len >= 0 && (long long)c1 <= a.tokens &&
          (a.mode == MODE_CAUSAL || (len & 1) == 0) && n <= a.n;
+}
+
+// Softcapping in base-2 units: for a raw score x (q.k, before the scale),
+// e = 2^(x * in) = exp(2 s / cap) with s = scale * x, r = 1 / (e + 1), and
+// the capped score in base 2 is out * (1 - 2 r) = cap * tanh(s / cap) * log2(e);
+// its derivative with respect to s is 1 - tanh^2 = 4 r (1 - r).
+struct Softcap {
+  float in, out;
+};
+__device__ __forceinline__ Softcap softcap_consts(float scale, float cap) {
+  return Softcap{scale / cap * 2.f * 1.4426950408889634f, cap * 1.4426950408889634f};
+}
+__device__ __forceinline__ float softcap_r(const Softcap& c, float x) {
+  return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x * c.in) + 1.f);
+}
+__device__ __forceinline__ float softcap_y(const Softcap& c, float r) {
+  return __builtin_fmaf(-2.f * c.out, r, c.out);
 }
 
 // Each returns hipSuccess or the launch error.

@@ -103,8 +103,8 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
  * for the batched layout (n = half length, or S; total_tokens ignored),
  * non-NULL for packed samples (n = the longest, total_tokens as in the
  * varlen entry points); H_kv = H for plain multi-head attention; mode 0 =
- * diffusion with block_size, 1 = causal (block_size ignored); workspace as
- * the matching *_workspace_size function gives.
+ * diffusion with block_size, 1 = causal (block_size ignored); softcap as
+ * in bdattn_fwd (0: off); workspace as bdattn_bwd_workspace_size gives.
  *   stage 0 -- dQ; it also writes the per-row -delta_i = -(dout_i . out_i)
  *              and lse_i * log2(e) to the workspace;
  *   stage 1 -- dK and dV (reads the workspace written by stage 0; with
@@ -116,8 +116,8 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
 int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, const int32_t* cu_seqlens, int B, int n, int total_tokens, int H,
-                     int H_kv, int D, int block_size, float scale, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     int H_kv, int D, int block_size, float scale, float softcap,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal yardstick forward: q, k, v, out [B][S][H][D] bf16, lse [B][H][S] fp32. */
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -246,6 +246,36 @@ int causal_attn_varlen_bwd(const void* q, const void* k, const void* v, const vo
                            const int32_t* cu_seqlens, int B, int max_S, int total_tokens, int H,
                            int H_kv, int D, float scale, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * The general form of the bf16 passes: every option in one call.
+ *   mode        : 0 = block diffusion (T = 2n, block_size), 1 = causal (T = n)
+ *   cu_seqlens  : NULL for the batched layout [B][T][heads][D] (n = half or
+ *                 sequence length, total_tokens ignored); non-NULL for
+ *                 packed samples as in the varlen entry points (n = the
+ *                 longest; total_tokens = 0 computes nothing)
+ *   H, H_kv     : query and key/value heads (grouped as in the _gqa entry
+ *                 points; H_kv = H for plain multi-head attention)
+ *   softcap     : 0 = off; > 0 caps the scaled scores s to
+ *                 softcap * tanh(s / softcap) before the softmax (the
+ *                 softcapping Fast Diffusion Attention lists among what its
+ *                 tests cover, "Accuracy"; defined as in flash-attention),
+ *                 and the backward takes the cap's derivative into dS.
+ *                 Must be finite and >= 0.
+ * Tensors, workspace and errors as in the specific entry points, which are
+ * this call with softcap = 0.  bdattn_bwd_workspace_size takes packed = 0
+ * or 1 for the two layouts (the workspace does not depend on softcap).
+ */
+int bdattn_fwd(int mode, const void* q, const void* k, const void* v, void* out, float* lse,
+               const int32_t* cu_seqlens, int B, int n, int total_tokens, int H, int H_kv, int D,
+               int block_size, float scale, float softcap, void* stream);
+size_t bdattn_bwd_workspace_size(int mode, int packed, int B, int n, int total_tokens, int H,
+                                 int H_kv, int D);
+int bdattn_bwd(int mode, const void* q, const void* k, const void* v, const void* out,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               const int32_t* cu_seqlens, int B, int n, int total_tokens, int H, int H_kv, int D,
+               int block_size, float scale, float softcap, void* workspace,
+               size_t workspace_bytes, void* stream);
 
 /*
  * Host-side inspection of the tile enumeration the kernels use (pure integer

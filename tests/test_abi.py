@@ -84,7 +84,7 @@ def test_bwd_rejects(kw, want):
 def test_bwd_stage_rejects_unknown_stage(stage):
     # stage 0 is dQ (with the row statistics), stage 1 dK/dV; nothing else
     lib = bd.lib()
-    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), None, 1, 16, 0, 1, 1, 64, 4, 0.125, FAKE, 1 << 20, None) == INVALID
+    assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), None, 1, 16, 0, 1, 1, 64, 4, 0.125, 0.0, FAKE, 1 << 20, None) == INVALID
 
 
 def test_causal_rejects():
@@ -121,7 +121,7 @@ def test_grouped_entry_points_reject_bad_kv_heads(H, H_kv):
     assert lib.causal_attn_fwd_gqa(*([FAKE] * 5), 1, 16, H, H_kv, 64, 0.125, None) == INVALID
     assert lib.causal_attn_bwd_gqa(*([FAKE] * 9), 1, 16, H, H_kv, 64, 0.125, FAKE, 1 << 20,
                                    None) == INVALID
-    assert lib.bdattn_bwd_stage(0, 0, *([FAKE] * 9), None, 1, 16, 0, H, H_kv, 64, 4, 0.125, FAKE, 1 << 20,
+    assert lib.bdattn_bwd_stage(0, 0, *([FAKE] * 9), None, 1, 16, 0, H, H_kv, 64, 4, 0.125, 0.0, FAKE, 1 << 20,
                                 None) == INVALID
 
 
@@ -243,3 +243,24 @@ def test_fp8_forward_rejects_bad_arguments():
     assert f(H_kv=3) == INVALID
     assert lib.causal_attn_fwd_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 4, 64, 0.1,
                                    None) == INVALID
+
+
+def test_general_entry_points_check_softcap_and_mode():
+    lib = bd.lib()
+    fwd = lambda mode=0, cap=0.0: lib.bdattn_fwd(mode, *([FAKE] * 5), None, 1, 16, 0, 2, 2, 64, 4, 0.125, cap, None)
+    assert fwd(cap=-1.0) == INVALID
+    assert fwd(cap=float("nan")) == INVALID and fwd(cap=float("inf")) == INVALID
+    assert fwd(mode=2) == INVALID
+    bwd = lambda cap: lib.bdattn_bwd(0, *([FAKE] * 9), None, 1, 16, 0, 2, 2, 64, 4, 0.125, cap, FAKE, 1 << 20, None)
+    assert bwd(-0.5) == INVALID
+    # packed with no tokens: nothing to do
+    assert lib.bdattn_fwd(0, *([FAKE] * 5), FAKE, 3, 0, 0, 2, 2, 64, 4, 0.125, 1.0, None) == OK
+
+
+def test_general_workspace_size_matches_the_specific_ones():
+    W = bd.bdattn_bwd_workspace_size
+    assert W(0, 0, 2, 100, 0, 8, 2, 64) == bd.diffusion_attn_bwd_gqa_workspace_size(2, 100, 8, 2, 64)
+    assert W(1, 0, 2, 100, 0, 8, 8, 128) == bd.causal_attn_bwd_workspace_size(2, 100, 8, 128)
+    assert W(0, 1, 5, 300, 1234, 8, 2, 64) == bd.diffusion_attn_varlen_bwd_workspace_size(5, 300, 1234, 8, 2, 64)
+    assert W(1, 1, 5, 300, 1234, 4, 4, 64) == bd.causal_attn_varlen_bwd_workspace_size(5, 300, 1234, 4, 4, 64)
+    assert W(2, 0, 2, 100, 0, 8, 2, 64) == 0

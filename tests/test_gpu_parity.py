@@ -280,12 +280,12 @@ def test_backward_stages_in_order_on_two_streams():
     done0 = torch.cuda.Event()
     torch.cuda.synchronize()
     with torch.cuda.stream(s1):
-        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, ws,
+        bd.bdattn_bwd_stage(MD, 0, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, 0.0, ws,
                             stream=s1)
         done0.record(s1)
     s2.wait_event(done0)
     with torch.cuda.stream(s2):
-        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, ws,
+        bd.bdattn_bwd_stage(MD, 1, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, H, D, w.b, scale, 0.0, ws,
                             stream=s2)
     torch.cuda.synchronize()
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
@@ -822,3 +822,128 @@ def test_fp8_long_sequence_sampled():
             rows = np.arange(r0, r0 + 4096)
             check_fp8_head(out[bi, rows, h], lse[bi, h, rows], q, k, v, b, scale, rows,
                            f"fp8 long ({bi},{h}) rows {r0}..")
+
+
+# ---------------------------------------------------------------------------
+# Softcapping (scores s -> cap * tanh(s / cap)) through the general entry points
+# ---------------------------------------------------------------------------
+
+def run_general(mode, q, k, v, do, b, scale, softcap, cu=None, max_n=None):
+    """Forward and backward through bdattn_fwd / bdattn_bwd; batched tensors
+    (B, T, heads, D) when cu is None, packed (total, heads, D) otherwise."""
+    dev = _dev()
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    Hkv = k.shape[-2]
+    if cu is None:
+        B, T, H, D = q.shape
+        n = T // 2 if mode == bd.MODE_DIFFUSION else T
+        total, cu_t = 0, None
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        total, H, D = q.shape
+        B, n = len(cu) - 1, max_n
+        cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+        lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bd.bdattn_fwd(mode, q, k, v, out, lse, cu_t, B, n, total, H, Hkv, D, b, scale, softcap)
+    wsb = bd.bdattn_bwd_workspace_size(mode, cu is not None, B, n, total, H, Hkv, D)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    bd.bdattn_bwd(mode, q, k, v, out, do, lse, dq, dk, dv, cu_t, B, n, total, H, Hkv, D, b, scale, softcap,
+                  ws, wsb)
+    torch.cuda.synchronize()
+    res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    return {key: t.cpu() for key, t in res.items()}
+
+
+SOFTCAP_SHAPES = [  # B, n, H, H_kv, D, b, cap
+    (2, 100, 2, 2, 64, 16, 5.0), (1, 129, 4, 2, 128, 7, 1.0), (2, 300, 4, 1, 64, 64, 2.5),
+    (1, 64, 2, 2, 128, 200, 0.5), (1, 257, 8, 2, 128, 32, 20.0),
+]
+
+
+@pytest.mark.parametrize("B,n,H,Hkv,D,b,cap", SOFTCAP_SHAPES)
+def test_softcap_small(B, n, H, Hkv, D, b, cap):
+    """Grouped or not, split groups or not, caps from strong (0.5) to mild
+    (20): against the oracle with the same cap.  Inputs are scaled up so
+    that the cap bites."""
+    q, k, v, do = make_inputs(B, n, H, D, seed=10100 + n + D, H_kv=Hkv)
+    q = (q.float() * 3).to(torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    res = run_general(bd.MODE_DIFFUSION, q, k, v, do, b, scale, cap)
+    f = oracle.to_f64
+    O, L = oracle.grouped_forward(oracle.diffusion_forward, f(q), f(k), f(v), b=b, scale=scale, softcap=cap)
+    G = oracle.grouped_backward(oracle.diffusion_backward, f(q), f(k), f(v), f(do), b=b, scale=scale,
+                                softcap=cap)
+    tag = f"softcap {cap} n{n} H{H}/{Hkv} D{D} b{b}"
+    check_fwd(res["out"], res["lse"], O, L, tag)
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, tag)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_softcap_causal_and_varlen(D):
+    cap, scale = 2.0, -0.3  # a negative scale too: the cap keeps its sign
+    q, k, v, do = make_inputs(2, 150, 2, D, seed=10200 + D)
+    q = (q.float() * 3).to(torch.bfloat16)
+    cq, ck, cv, cdo = (make_causal_view(x) for x in (q, k, v, do))
+    res = run_general(bd.MODE_CAUSAL, cq, ck, cv, cdo, 1, scale, cap)
+    f = oracle.to_f64
+    O, L = oracle.batched(oracle.causal_forward, f(cq), f(ck), f(cv), scale=scale, softcap=cap)
+    G = oracle.batched(oracle.causal_backward, f(cq), f(ck), f(cv), f(cdo), scale=scale, softcap=cap)
+    check_fwd(res["out"], res["lse"], O, L, f"softcap causal D{D}")
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, f"softcap causal D{D}")
+    ns = [70, 0, 129, 33]
+    pq, pk, pv, pdo, cu = make_varlen_inputs(ns, 4, D, seed=10300 + D, H_kv=2)
+    pq = (pq.float() * 3).to(torch.bfloat16)
+    res = run_general(bd.MODE_DIFFUSION, pq, pk, pv, pdo, 8, scale, cap, cu=cu, max_n=max(ns))
+    O, L = oracle.varlen_forward(oracle.diffusion_forward, f(pq), f(pk), f(pv), cu, b=8, scale=scale,
+                                 softcap=cap)
+    G = oracle.varlen_backward(oracle.diffusion_backward, f(pq), f(pk), f(pv), f(pdo), cu, b=8,
+                               scale=scale, softcap=cap)
+    check_fwd(res["out"], res["lse"], O, L, f"softcap varlen D{D}")
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, f"softcap varlen D{D}")
+
+
+def test_general_entry_points_without_softcap_are_the_specific_ones():
+    q, k, v, do = make_inputs(2, 200, 4, 128, seed=10400, H_kv=2)
+    g = run_general(bd.MODE_DIFFUSION, q, k, v, do, 8, 0.1, 0.0)
+    s_ = run_grouped(q, k, v, do, 8, 0.1)
+    for key in g:
+        assert torch.equal(g[key], s_[key]), key
+
+
+def test_softcap_workload_heads():
+    """The short-sequence workload with a cap of 2 (c2: B=4, n=1024, H=16,
+    D=64, b=4), whole heads.  Its scaled scores reach about +-4, so the cap
+    bites (tanh(2) = 0.96) while the inputs keep the workload's N(0, 1)
+    draws, the regime the forward tolerance is stated for."""
+    w = WORKLOADS["c2"]
+    q, k, v, do = make_workload_inputs(w)
+    scale = 1 / math.sqrt(w.D)
+    cap = 2.0
+    res = run_general(bd.MODE_DIFFUSION, q, k, v, do, w.b, scale, cap)
+    f = oracle.to_f64
+    for bi, hi in ((0, 0), (3, 15)):
+        sl = lambda x: f(x[bi:bi + 1, :, hi:hi + 1])
+        O, L = oracle.batched(oracle.diffusion_forward, sl(q), sl(k), sl(v), b=w.b, scale=scale, softcap=cap)
+        G = oracle.batched(oracle.diffusion_backward, sl(q), sl(k), sl(v), sl(do), b=w.b, scale=scale,
+                           softcap=cap)
+        pick = lambda t: t[bi:bi + 1, :, hi:hi + 1]
+        check_fwd(pick(res["out"]), res["lse"][bi:bi + 1, hi:hi + 1], O, L, f"softcap c2 ({bi},{hi})")
+        for name, ref in zip(("dq", "dk", "dv"), G):
+            check_grad(pick(res[name]), ref, name, f"softcap c2 ({bi},{hi})")
+
+
+def test_softcap_autograd():
+    dev = _dev()
+    q, k, v, do = make_inputs(1, 96, 2, 64, seed=10500)
+    ref = run_general(bd.MODE_DIFFUSION, q, k, v, do, 4, 0.125, 3.0)
+    tq, tk, tv = (x.to(dev).requires_grad_() for x in (q, k, v))
+    out, lse = bd.diffusion_attn_func(tq, tk, tv, 4, softmax_scale=0.125, return_lse=True, softcap=3.0)
+    out.backward(do.to(dev))
+    assert torch.equal(out.detach().cpu(), ref["out"])
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert torch.equal(t.grad.cpu(), ref[name]), name
