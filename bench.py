@@ -63,6 +63,8 @@ def parse():
                     help="folder holding traffic_<kernel>_<workload>.txt (HBM bytes per launch)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="cap the scores to softcap * tanh(s / softcap) (batched workloads; 0: off)")
     ap.add_argument("--fp8", action="store_true",
                     help="time the FP8 (E4M3) forward pass instead (batched workloads)")
     return ap.parse_args()
@@ -191,8 +193,9 @@ def mark(ev, i):
         ev[i].record()
 
 
-def setup_batched(w, dev, torch, bd):
-    """(B, 2n, H, D) tensors; the yardstick views them as (2B, n, H, D)."""
+def setup_batched(w, dev, torch, bd, softcap=0.0):
+    """(B, 2n, H, D) tensors; the yardstick views them as (2B, n, H, D).
+    softcap > 0 runs both through the general entry points with that cap."""
     from workloads import make_workload_inputs
     B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
     scale = 1.0 / math.sqrt(D)
@@ -216,26 +219,30 @@ def setup_batched(w, dev, torch, bd):
 
     def diffusion_step(ev=None):
         mark(ev, 0)
-        if Hkv == H:
+        if softcap:
+            bd.bdattn_fwd(MD, q, k, v, out, lse, None, B, n, 0, H, Hkv, D, b, scale, softcap)
+        elif Hkv == H:
             bd.diffusion_attn_fwd(q, k, v, out, lse, B, n, H, D, b, scale)
         else:
             bd.diffusion_attn_fwd_gqa(q, k, v, out, lse, B, n, H, Hkv, D, b, scale)
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MD, stage, q, k, v, out, do, lse, dq, dk, dv, None, B, n, 0, H, Hkv, D, b,
-                                scale, 0.0, ws, ws_bytes)
+                                scale, softcap, ws, ws_bytes)
             mark(ev, 2 + stage)
 
     def causal_step(ev=None):
         mark(ev, 0)
-        if Hkv == H:
+        if softcap:
+            bd.bdattn_fwd(MC, cq, ck, cv, cout, clse, None, 2 * B, n, 0, H, Hkv, D, 1, scale, softcap)
+        elif Hkv == H:
             bd.causal_attn_fwd(cq, ck, cv, cout, clse, 2 * B, n, H, D, scale)
         else:
             bd.causal_attn_fwd_gqa(cq, ck, cv, cout, clse, 2 * B, n, H, Hkv, D, scale)
         mark(ev, 1)
         for stage in range(2):
             bd.bdattn_bwd_stage(MC, stage, cq, ck, cv, cout, cdo, clse, cdq, cdk, cdv, None, 2 * B, n, 0,
-                                H, Hkv, D, 1, scale, 0.0, cws)
+                                H, Hkv, D, 1, scale, softcap, cws)
             mark(ev, 2 + stage)
 
     def ungrouped():
@@ -275,7 +282,8 @@ def setup_batched(w, dev, torch, bd):
     return Problem(diffusion_step=diffusion_step, causal_step=causal_step, ungrouped=ungrouped,
                    cpu_heads=cpu_heads, pair_heads=P * H * B, causal_pair_heads=n * (n + 1) // 2 * H * 2 * B,
                    config={"workload": w.describe(), "global_batch": B, "seq_len": 2 * n, "block_size": b,
-                           "heads": H, "kv_heads": Hkv, "headdim": D, "parallelism": "single-gpu"})
+                           "heads": H, "kv_heads": Hkv, "headdim": D, "softcap": softcap,
+                           "parallelism": "single-gpu"})
 
 
 def setup_varlen(w, dev, torch, bd):
@@ -459,7 +467,10 @@ def main():
             sys.exit(2)
         print(json.dumps(bench_fp8(args, w, dev, torch, bd)))
         return
-    prob = setup(w, dev, torch, bd)
+    if args.softcap and setup is not setup_batched:
+        print("--softcap takes a batched workload", file=sys.stderr)
+        sys.exit(2)
+    prob = setup_batched(w, dev, torch, bd, args.softcap) if args.softcap else setup(w, dev, torch, bd)
     D = w.D
 
     # ---- warm-up, then exactly K timed steps --------------------------------
