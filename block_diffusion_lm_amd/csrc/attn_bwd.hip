@@ -282,6 +282,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     // -delta, so that the chain yields dP - delta.
     auto product1 = [&](const uint16_t* Tb, const bool (&act)[C::QB], floatx16 (&t)[C::QB], auto init)
         __attribute__((always_inline)) {
+      mfma_burst_begin();
       if (act[0] && act[1]) {
         constexpr int PF = 2;
         t[0] = init(0);
@@ -311,11 +312,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
           for (int s = 0; s < C::KS; ++s) t[qb] = mfma32(lds_vec_at(Tb + 32 * qb * D + xoff[s]), xf[s], t[qb]);
         }
       }
+      mfma_burst_end();
     };
     // Second product: dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave)
     // for block qb of the tile at Tb, B operand halves bop.
     auto product2 = [&](const uint16_t* Tb, auto qbc, const bf16x8 (&bop)[2]) __attribute__((always_inline)) {
       constexpr int qb = decltype(qbc)::value;
+      mfma_burst_begin();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const uint16_t* yr = Tb + (32 * qb + 16 * ks) * D;
@@ -323,6 +326,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
         for (int db = 0; db < C::DB; ++db)
           acc[db] = mfma32(lds_trA_at(yr + yoff[db][0], yr + yoff[db][1]), bop[ks], acc[db]);
       }
+      mfma_burst_end();
     };
 
     // dS-wave: dP of the previous tile and which of its blocks are active
@@ -701,6 +705,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           ak[s] = lds_vec_at(Ks + 32 * kb * D + roff[s]);
           av[s] = lds_vec_at(Vs + 32 * kb * D + roff[s]);
         }
+        mfma_burst_begin();
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
           if (s + PF < C::KS) {
@@ -711,6 +716,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           dp = mfma32(av[s], gf[s], dp);
           __builtin_amdgcn_sched_barrier(0);
         }
+        mfma_burst_end();
         // P^T = exp2(S^T * scale * log2 e - LSE * log2 e), dS^T = P^T (dP^T - delta)
         if constexpr (SC) {
           // sp becomes P (1 - tanh^2): all that dS needs
@@ -737,6 +743,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
         for (int r = 0; r < 16; ++r) dp[r] = sp[r] * (dp[r] + ndlt);
         const bf16x8 sb0 = pack_bf16x8(dp, 0), sb1 = pack_bf16x8(dp, 8);
         // dQ^T += K^T dS^T
+        mfma_burst_begin();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const uint16_t* kr = Ks + (32 * kb + 16 * ks) * D;
@@ -744,6 +751,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) 
           for (int db = 0; db < C::DB; ++db)
             dq[db] = mfma32(lds_trA_at(kr + toff[db][0], kr + toff[db][1]), ks ? sb1 : sb0, dq[db]);
         }
+        mfma_burst_end();
       }
     }
 

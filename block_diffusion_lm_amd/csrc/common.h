@@ -73,11 +73,12 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Issue priority of the wave around a burst of MFMAs.  A wave's own vector
-// ALU work does not overlap its MFMAs (measured on MI355X), so throughput
-// comes from the other wave on the SIMD running its softmax arithmetic
-// meanwhile; raising the priority of the wave that is in an MFMA burst keeps
-// the matrix core fed while the other wave fills the remaining issue slots.
+// Issue priority of the wave around a burst of MFMAs (compiled in with
+// BDATTN_SETPRIO).  A wave's own vector ALU work does not overlap its MFMAs
+// (measured on MI355X), so throughput comes from the other wave on the SIMD
+// running its softmax arithmetic meanwhile; raising the priority of the wave
+// in an MFMA burst was meant to keep the matrix core fed, but measured 3-5%
+// slower in every kernel, so it is off by default.
 #ifdef BDATTN_SETPRIO
 __device__ __forceinline__ void mfma_burst_begin() { __builtin_amdgcn_s_setprio(1); }
 __device__ __forceinline__ void mfma_burst_end() { __builtin_amdgcn_s_setprio(0); }
