@@ -448,9 +448,9 @@ def main():
 
     import torch
     import block_diffusion_lm_amd as bd
-    from workloads import GQA_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS
+    from workloads import GQA_WORKLOADS, HEAD_DIM_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS
 
-    batched = {**WORKLOADS, **GQA_WORKLOADS}
+    batched = {**WORKLOADS, **GQA_WORKLOADS, **HEAD_DIM_WORKLOADS}
     if args.workload in batched:
         w, setup = batched[args.workload], setup_batched
     elif args.workload in VARLEN_WORKLOADS:

@@ -49,22 +49,17 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
 }
 
 // Per-segment scalars.  A key-stationary wave needs, for each query half it
-// walks: the rows that see its first and last keys (query-block
-// classification), the rows that see this lane's key (element mask), and the
-// offsets of row 0 of Q / dO and of its statistics.  A query-stationary wave
-// needs the visible intervals of its first, last and own rows and the offset
-// of row 0 of K / V.  They are kept as separate scalars and picked with
-// selects: grouped in a struct, the compiler would select between the
-// structs' addresses and keep both in scratch memory.
+// walks, the rows that see this lane's key (element mask), the offsets of
+// row 0 of Q / dO and of its statistics, and the rows that see its first and
+// last keys (query-block classification).  A query-stationary wave needs the
+// visible intervals of its first, last and own rows and the offset of row 0
+// of K / V.  They are kept as separate scalars and picked with selects:
+// grouped in a struct, the compiler would select between the structs'
+// addresses and keep both in scratch memory.
 #define COL_SEGMENTS                                                          \
   const size_t stat_base = stat0 + (size_t)hh0 * a.stat_hs;                  \
-  int clo_f0, chi_f0, clo_l0, chi_l0, clo_p0, chi_p0;                        \
-  int clo_f1, chi_f1, clo_l1, chi_l1, clo_p1, chi_p1;                        \
-  col_interval(g, seg.half0, kh, kw0, clo_f0, chi_f0);                        \
-  col_interval(g, seg.half0, kh, max(kw1 - 1, kw0), clo_l0, chi_l0);          \
+  int clo_p0, chi_p0, clo_p1, chi_p1;                                        \
   col_interval(g, seg.half0, kh, key, clo_p0, chi_p0);                        \
-  col_interval(g, seg.half1, kh, kw0, clo_f1, chi_f1);                        \
-  col_interval(g, seg.half1, kh, max(kw1 - 1, kw0), clo_l1, chi_l1);          \
   col_interval(g, seg.half1, kh, key, clo_p1, chi_p1);                        \
   const size_t qb0 = (sample0 + half_off(a, seg.half0, n)) * rs + (size_t)hh0 * D; \
   const size_t qb1 = (sample0 + half_off(a, seg.half1, n)) * rs + (size_t)hh0 * D; \
@@ -94,12 +89,14 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
 // P-waves' tile, the dS-waves' tile and the tile in flight, and the P
 // exchange is double-buffered.
 // ---------------------------------------------------------------------------
+// D = 256: two pairs (one wave per SIMD, each with the whole register
+// file) and 32-row query tiles, so that the three-deep Q / dO ring fits LDS.
 template <int D>
 struct DkdvCfg {
-  static constexpr int NPAIR = 4;
-  static constexpr int NT = 128 * NPAIR;  // 8 waves
+  static constexpr int NPAIR = D == 256 ? 2 : 4;
+  static constexpr int NT = 128 * NPAIR;  // 8 waves (4 at D = 256)
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
-  static constexpr int BQ = 64;           // query rows per streamed tile
+  static constexpr int BQ = D == 256 ? 32 : 64;  // query rows per streamed tile
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -109,7 +106,9 @@ struct DkdvCfg {
   // tile, and the barrier that ends the step publishes it to the dS-waves.
   using Tile = DirectTile<BQ, D, NT / 2>;
   static constexpr int BUF = 2 * Tile::ELEMS;   // Q then dO
-  static constexpr int FBUF = 2 * BQ;           // lse2 then -delta
+  // lse2 then -delta, each loaded by one wave-wide instruction (64 floats)
+  static constexpr int STATW = 64;
+  static constexpr int FBUF = 2 * STATW;
   static constexpr int PXS = NPAIR * QB * 2 * 64;  // 16-byte slots of one P exchange buffer
 };
 
@@ -119,7 +118,7 @@ struct DkdvCfg {
 // P-wave recomputes P from the capped scores and publishes
 // P (1 - tanh^2), so that the dS-wave's dS carries the cap's derivative).
 template <int D, bool GROUPED, bool SC>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
+__global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
   using C = DkdvCfg<D>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NBUF * C::BUF];
@@ -131,8 +130,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wv & 3;
-  const bool pwave = wv < 4;
+  const int pair = wv % C::NPAIR;
+  const bool pwave = wv < C::NPAIR;
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
@@ -194,6 +193,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
   const int nsteps = gs * ntiles;
   auto head_of_step = [&](int t) -> int { return (!GROUPED || gs == 1) ? 0 : t / ntiles; };
   COL_SEGMENTS
+  // the blocks of the pair's first and last keys
+  const int kblk_f0 = g.bstart(kw0), kblk_f1 = g.bend(kw0);
+  const int kblk_l0 = g.bstart(max(kw1 - 1, kw0)), kblk_l1 = g.bend(max(kw1 - 1, kw0));
+  int clo_f0, chi_f0, clo_l0, chi_l0, clo_f1, chi_f1, clo_l1, chi_l1;
+  col_interval_of_block(n, seg.half0, kh, kblk_f0, kblk_f1, clo_f0, chi_f0);
+  col_interval_of_block(n, seg.half0, kh, kblk_l0, kblk_l1, clo_l0, chi_l0);
+  col_interval_of_block(n, seg.half1, kh, kblk_f0, kblk_f1, clo_f1, chi_f1);
+  col_interval_of_block(n, seg.half1, kh, kblk_l0, kblk_l1, clo_l1, chi_l1);
   auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int gi = head_of_step(t);
     const int i = t - gi * ntiles;
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     if (wv == 0)
       lds_direct4(make_rsrc(a.lse2 + sb, sbytes), fdst, (uint32_t)lane * 4u, (uint32_t)qt * C::BQ * 4u);
     if (wv == 1)
-      lds_direct4(make_rsrc(a.ndelta + sb, sbytes), fdst + C::BQ * 4u, (uint32_t)lane * 4u,
+      lds_direct4(make_rsrc(a.ndelta + sb, sbytes), fdst + C::STATW * 4u, (uint32_t)lane * 4u,
                   (uint32_t)qt * C::BQ * 4u);
   };
 
@@ -247,9 +254,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u) yoff[db][u] = ysel + trA_lane_off<D>(lane, 32 * db, u);
-    using Q0 = std::integral_constant<int, 0>;
-    using Q1 = std::integral_constant<int, 1>;
-    static_assert(C::QB == 2, "two 32-row blocks per query tile");
 
     // Which 32-row blocks of tile i see some key of the pair (act) or every
     // key of it (full); qt, and the rows [clo, chi) that see this lane's key.
@@ -258,8 +262,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
       const int i = t - head_of_step(t) * ntiles;
       const bool second = i >= n0;
       qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-      const int cf = second ? clo_f1 : clo_f0, hf = second ? chi_f1 : chi_f0;
-      const int cl = second ? clo_l1 : clo_l0, hl = second ? chi_l1 : chi_l0;
+      // The pair's intervals for the tile's half.  At D = 256 they are
+      // derived here: selected from the two halves' copies, they ended up
+      // read through a table of addresses in scratch memory.  (The copies
+      // measured slightly faster at the other widths.)
+      int cf, hf, cl, hl;
+      if constexpr (D == 256) {
+        const int qh = second ? seg.half1 : seg.half0;
+        col_interval_of_block(n, qh, kh, kblk_f0, kblk_f1, cf, hf);
+        col_interval_of_block(n, qh, kh, kblk_l0, kblk_l1, cl, hl);
+      } else {
+        cf = second ? clo_f1 : clo_f0;
+        hf = second ? chi_f1 : chi_f0;
+        cl = second ? clo_l1 : clo_l0;
+        hl = second ? chi_l1 : chi_l0;
+      }
       clo = second ? clo_p1 : clo_p0;
       chi = second ? chi_p1 : chi_p0;
 #pragma unroll
@@ -283,7 +300,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
     auto product1 = [&](const uint16_t* Tb, const bool (&act)[C::QB], floatx16 (&t)[C::QB], auto init)
         __attribute__((always_inline)) {
       mfma_burst_begin();
-      if (act[0] && act[1]) {
+      if constexpr (C::QB == 2) {
+        if (act[0] && act[1]) {
         constexpr int PF = 2;
         t[0] = init(0);
         t[1] = init(1);
@@ -303,14 +321,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
           t[1] = mfma32(a1[s], xf[s], t[1]);
           __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) {
-          if (!act[qb]) continue;
-          t[qb] = init(qb);
-#pragma unroll
-          for (int s = 0; s < C::KS; ++s) t[qb] = mfma32(lds_vec_at(Tb + 32 * qb * D + xoff[s]), xf[s], t[qb]);
+        mfma_burst_end();
+        return;
         }
+      }
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        if (!act[qb]) continue;
+        t[qb] = init(qb);
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) t[qb] = mfma32(lds_vec_at(Tb + 32 * qb * D + xoff[s]), xf[s], t[qb]);
       }
       mfma_burst_end();
     };
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
 
     // dS-wave: dP of the previous tile and which of its blocks are active
     floatx16 dpr[C::QB];
-    bool pact[C::QB] = {false, false};
+    bool pact[C::QB] = {};
     // Step j; tile j sits in ring slot SLOT = j mod NBUF, a compile-time
     // constant (the loop below is unrolled by the ring depth) so that every
     // LDS read is a lane register plus an immediate offset.
@@ -404,8 +424,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
             }
             product2(Tb, qbc, bop);
           };
-          step(Q0{});
-          step(Q1{});
+          static_for<C::QB>(step);
         }
       } else {
         if (j >= 1) {
@@ -429,15 +448,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
             const bf16x8 bop[2] = {pack_bf16x8(x, 0), pack_bf16x8(x, 8)};
             product2(Tb, qbc, bop);
           };
-          step(Q0{});
-          step(Q1{});
+          static_for<C::QB>(step);
         }
         if (j < nsteps) {
           bool full[C::QB];
           int qt, clo, chi;
           blocks(j, pact, full, qt, clo, chi);
           // register r of block qb holds row 32 qb + 8 (r / 4) + 4 h2 + r % 4
-          const float* Nd = fsm + slot * C::FBUF + C::BQ;
+          const float* Nd = fsm + slot * C::FBUF + C::STATW;
           product1(smem + slot * C::BUF, pact, dpr, [&](int qb) {
             floatx16 z;
 #pragma unroll
@@ -451,7 +469,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles
             return z;
           });
         } else {
-          pact[0] = pact[1] = false;
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) pact[qb] = false;
         }
       }
       wait_vmem();
@@ -550,7 +569,7 @@ struct DqCfg {
 
 // SC: softcapping on (P from the capped scores, dS times 1 - tanh^2).
 template <int D, bool SC>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(AttnArgs a, int qtiles) {
+__global__ __launch_bounds__(256, (D < 256 ? 2 : 1)) void bwd_dq_kernel(AttnArgs a, int qtiles) {
   using C = DqCfg<D>;
   using Tile = typename C::Tile;
   constexpr int BN = C::BN;
@@ -818,9 +837,10 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
 // (4 per CU on 256 CUs).
 constexpr long long kDkdvMinBlocks = 1024;
 
-int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G) {
-  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV, "one key tile size for both widths");
-  const long long ktiles = ((long long)n + DkdvCfg<128>::BKV - 1) / DkdvCfg<128>::BKV;
+int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
+  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV, "one key tile size for D = 64 and 128");
+  const int bkv = D == 256 ? DkdvCfg<256>::BKV : DkdvCfg<128>::BKV;
+  const long long ktiles = ((long long)n + bkv - 1) / bkv;
   const long long base = ktiles * nhalves * B * Hkv;
   int S = 1;
   for (int c = 1; c <= G; ++c) {
@@ -832,7 +852,9 @@ int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G) {
 }
 
 hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s) {
-  return D == 64 ? launch_stage_t<64>(a, stage, s) : launch_stage_t<128>(a, stage, s);
+  if (D == 64) return launch_stage_t<64>(a, stage, s);
+  if (D == 256) return launch_stage_t<256>(a, stage, s);
+  return launch_stage_t<128>(a, stage, s);
 }
 
 hipError_t launch_bwd(const AttnArgs& a, int D, hipStream_t s) {

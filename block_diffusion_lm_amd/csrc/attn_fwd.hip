@@ -60,7 +60,8 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // SC: softcapping on (the scores are capped before the mask and the
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
-__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
+// D = 256 holds Q and O in one wave's full register file (occupancy 1).
+__global__ __launch_bounds__(64 * NW, (NW == 4 && D < 256 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
@@ -320,6 +321,7 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
   if (D == 64) return launch_fwd_t<64, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  if (D == 256) return launch_fwd_t<256, 64, 4, 2>(a, s);
   return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }
 

@@ -64,21 +64,27 @@ BD_HD void row_interval(const Geom& g, int qh, int kh, int p, int& lo, int& hi) 
   }
 }
 
-// Query rows of half qh that see key c of half kh: [lo, hi).
-BD_HD void col_interval(const Geom& g, int qh, int kh, int c, int& lo, int& hi) {
+// Query rows of half qh that see a key of half kh whose block is
+// [bs, be): [lo, hi).
+BD_HD void col_interval_of_block(int n, int qh, int kh, int bs, int be, int& lo, int& hi) {
   if (kh == NOISY && qh == NOISY) {
-    lo = g.bstart(c);
-    hi = g.bend(c);
+    lo = bs;
+    hi = be;
   } else if (kh == CLEAN && qh == NOISY) {  // noisy rows of later blocks
-    lo = g.bend(c);
-    hi = g.n;
+    lo = be;
+    hi = n;
   } else if (kh == CLEAN) {                 // clean rows of the same or later blocks
-    lo = g.bstart(c);
-    hi = g.n;
+    lo = bs;
+    hi = n;
   } else {
     lo = 0;
     hi = 0;
   }
+}
+
+// Query rows of half qh that see key c of half kh: [lo, hi).
+BD_HD void col_interval(const Geom& g, int qh, int kh, int c, int& lo, int& hi) {
+  col_interval_of_block(g.n, qh, kh, g.bstart(c), g.bend(c), lo, hi);
 }
 
 // Classify the rectangle rows [r0, r1) x keys [c0, c1) (r0 < r1 <= n,

@@ -71,7 +71,7 @@ __device__ __forceinline__ void query_head(const AttnArgs& a, int x, int& bi, in
 // over: 1 (one workgroup walks the whole group) unless that leaves fewer
 // than a few workgroups per CU; then the smallest divisor of G that does
 // not.  Above 1 the workgroups write float32 partials that a reduction sums.
-int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G);
+int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D);
 
 // Sample bi: the token index of its first token, its half length n
 // (sequence length in causal mode) and the index of its statistics for

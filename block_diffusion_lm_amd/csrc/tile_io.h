@@ -4,8 +4,9 @@
 // LDS directly (no staging registers).  The buffer resource of a tile
 // covers exactly the rows of its half, so rows past the end of the half
 // read as zero.  In LDS a tile is row-major with no padding; the 16-byte
-// chunk c of row r sits at chunk c ^ swz(r).  swz permutes 0..7 over every
-// 8 consecutive rows, which makes two read patterns free of bank conflicts:
+// chunk c of row r sits at chunk c ^ swz(r).  swz permutes the chunks of
+// every group of consecutive rows so that two read patterns are free of
+// bank conflicts (64 banks of 4 bytes):
 //  * natural operand reads: 8 consecutive rows, one 16-byte chunk each
 //    (ds_read_b128), e.g. K as the A operand of S^T = K Q^T;
 //  * transposing reads (ds_read_b64_tr_b16): a 16-lane group reads 4
@@ -22,7 +23,9 @@ namespace bd {
 
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  // D >= 128: rows of 16 or 32 chunks; the permutation of 0..15 keeps both
+  // read patterns on distinct banks (D = 256 rows span two bank lines).
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

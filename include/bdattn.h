@@ -26,7 +26,8 @@
  *    Materialization, section 4.5: the statistic saved for the backward).
  *  - scale multiplies q.k before the softmax (callers usually pass
  *    1/sqrt(D)).  It must be finite and nonzero.
- *  - D must be 64 or 128.  B, n (or S), H >= 1.  block_size >= 1; a block
+ *  - D must be 64, 128 or 256 (the FP8 forward: 64 or 128).  B, n (or S),
+ *    H >= 1.  block_size >= 1; a block
  *    longer than a half is allowed (one block per half).  One sample's
  *    tensor (2n or S tokens x H x D bf16) must be smaller than 2 GiB
  *    (BDATTN_ERR_UNSUPPORTED otherwise).
@@ -53,7 +54,7 @@ extern "C" {
 enum {
   BDATTN_OK = 0,
   BDATTN_ERR_INVALID = 1,      /* null pointer, misaligned pointer, bad size or scale */
-  BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64 or 128 */
+  BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64, 128 or 256 */
   BDATTN_ERR_LAUNCH = 3,       /* the HIP runtime refused a launch */
 };
 
@@ -191,7 +192,8 @@ int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void*
  * the maximum).  T = 2n (diffusion, block_size as above) or S (causal).
  * Grouped heads as in the _gqa entry points.  Same pointer, size and
  * error rules as diffusion_attn_fwd, plus: the descale arrays must be
- * non-NULL and 4-byte aligned.  There is no FP8 backward.
+ * non-NULL and 4-byte aligned, and D must be 64 or 128
+ * (BDATTN_ERR_UNSUPPORTED for 256).  There is no FP8 backward.
  */
 int diffusion_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                            const float* k_descale, const float* v_descale, void* out, float* lse,

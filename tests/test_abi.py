@@ -55,7 +55,7 @@ def _fwd(**kw):
     (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(v=FAKE + 2), INVALID),
     (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(H=-1), INVALID), (dict(b=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
-    (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
+    (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=512), UNSUPPORTED),
     (dict(n=2 ** 22, H=2, D=128), UNSUPPORTED),
     # 2^31 rows in all (over the 32-bit row limit), each sample small
     (dict(B=2 ** 20, n=1024, H=1, D=64), INVALID),
@@ -145,10 +145,11 @@ def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     """Statistics (two float32 per query row) plus, when the dK/dV kernel
     splits the groups, float32 partial dK and dV per split.  The split count
     is the smallest divisor S of G = H / Hkv giving at least 1024 dK/dV
-    workgroups of 128 keys (all of G when none does)."""
+    workgroups of 128 keys, 64 at D = 256 (all of G when none does)."""
     T = n if causal else 2 * n
     r256 = lambda x: -(-x // 256) * 256
-    base = -(-n // 128) * (1 if causal else 2) * B * Hkv
+    bkv = 64 if D == 256 else 128
+    base = -(-n // bkv) * (1 if causal else 2) * B * Hkv
     G = H // Hkv
     S = next((c for c in range(1, G + 1) if G % c == 0 and base * c >= 1024), G)
     part = 2 * S * B * T * Hkv * D * 4 if S > 1 else 0
@@ -161,6 +162,8 @@ def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     (2, 100, 4, 2, 64),      # tiny: every query head on its own, S = G
     (1, 7, 8, 2, 128),
     (3, 5000, 12, 12, 64),   # plain multi-head
+    (2, 4096, 16, 2, 256),   # 512 workgroups of 64 keys: S = 2
+    (1, 1000, 8, 1, 256),
 ])
 def test_gqa_workspace_sizes(B, n, H, Hkv, D):
     want, S = _expected_gqa_workspace(B, n, H, Hkv, D)
@@ -240,6 +243,7 @@ def test_fp8_forward_rejects_bad_arguments():
     assert f(qd=None) == INVALID and f(kd=None) == INVALID and f(vd=None) == INVALID
     assert f(vd=FAKE + 2) == INVALID            # descales must be 4-byte aligned
     assert f(D=96) == UNSUPPORTED
+    assert f(D=256) == UNSUPPORTED              # no FP8 kernel at D = 256
     assert f(H_kv=3) == INVALID
     assert lib.causal_attn_fwd_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 4, 64, 0.1,
                                    None) == INVALID

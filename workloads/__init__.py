@@ -70,6 +70,13 @@ for _D in (64, 128):
         _w = _c5(_D, _b)
         WORKLOADS[_w.name] = _w
 
+# Head dimension 256: the block-size-sweep problem with half the heads at
+# twice the width (the same tokens, bytes and FLOPs as its D = 128, b = 48
+# member).
+HEAD_DIM_WORKLOADS: Dict[str, Workload] = {
+    "h1": Workload("h1", B=4, n=4096, H=8, D=256, b=48, seed=1031),
+}
+
 # Grouped-query problems (query heads sharing key/value heads): the
 # short-sequence regime in which the pages report the grouped backward's
 # gain (512 to 1K tokens per half), the long-sequence problem with four
