@@ -43,7 +43,7 @@ int check_problem(const Problem& p) {
   if (p.B < 1 || p.n < 1 || p.H < 1 || p.b < 1) return BDATTN_ERR_INVALID;
   if (p.mode == bd::MODE_DIFFUSION && p.n > std::numeric_limits<int>::max() / 2)
     return BDATTN_ERR_INVALID;
-  if (p.D != 64 && p.D != 128 && p.D != 256) return BDATTN_ERR_UNSUPPORTED;
+  if (p.D != 64 && p.D != 96 && p.D != 128 && p.D != 192 && p.D != 256) return BDATTN_ERR_UNSUPPORTED;
   if (p.Hkv < 1 || p.Hkv > p.H || p.H % p.Hkv != 0) return BDATTN_ERR_INVALID;
   if (p.packed() && (p.total < 1 || !aligned(p.cu, 4))) return BDATTN_ERR_INVALID;
   const long long T = p.T();
@@ -123,7 +123,7 @@ int run_fwd_fp8(const Problem& p, const void* q, const void* k, const void* v, c
   if (!aligned(qd, 4) || !aligned(kd, 4) || !aligned(vd, 4)) return BDATTN_ERR_INVALID;
   const int st = check_problem(p);
   if (st != BDATTN_OK) return st;
-  if (p.D == 256) return BDATTN_ERR_UNSUPPORTED;  // the FP8 forward takes D = 64 or 128
+  if (p.D != 64 && p.D != 128) return BDATTN_ERR_UNSUPPORTED;  // the FP8 forward takes D = 64 or 128
   bd::AttnArgs a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -199,7 +199,7 @@ const char* bdattn_status_string(int status) {
   switch (status) {
     case BDATTN_OK: return "ok";
     case BDATTN_ERR_INVALID: return "invalid argument";
-    case BDATTN_ERR_UNSUPPORTED: return "unsupported head dimension (need 64, 128 or 256) or size";
+    case BDATTN_ERR_UNSUPPORTED: return "unsupported head dimension (need 64, 96, 128, 192 or 256) or size";
     case BDATTN_ERR_LAUNCH: return "HIP launch error";
     default: return "unknown status";
   }

@@ -89,14 +89,16 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
 // P-waves' tile, the dS-waves' tile and the tile in flight, and the P
 // exchange is double-buffered.
 // ---------------------------------------------------------------------------
-// D = 256: two pairs (one wave per SIMD, each with the whole register
-// file) and 32-row query tiles, so that the three-deep Q / dO ring fits LDS.
+// D = 192 and 256 stream 32-row query tiles, so that the three-deep Q / dO
+// ring fits LDS; D = 256 also runs two pairs only (one wave per SIMD, each
+// with the whole register file), while D = 192 still fits two waves per SIMD.
 template <int D>
 struct DkdvCfg {
+  static constexpr bool WIDE = D >= 192;
   static constexpr int NPAIR = D == 256 ? 2 : 4;
   static constexpr int NT = 128 * NPAIR;  // 8 waves (4 at D = 256)
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
-  static constexpr int BQ = D == 256 ? 32 : 64;  // query rows per streamed tile
+  static constexpr int BQ = WIDE ? 32 : 64;  // query rows per streamed tile
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -262,12 +264,12 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(AttnArgs a,
       const int i = t - head_of_step(t) * ntiles;
       const bool second = i >= n0;
       qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-      // The pair's intervals for the tile's half.  At D = 256 they are
+      // The pair's intervals for the tile's half.  At D >= 192 they are
       // derived here: selected from the two halves' copies, they ended up
       // read through a table of addresses in scratch memory.  (The copies
       // measured slightly faster at the other widths.)
       int cf, hf, cl, hl;
-      if constexpr (D == 256) {
+      if constexpr (C::WIDE) {
         const int qh = second ? seg.half1 : seg.half0;
         col_interval_of_block(n, qh, kh, kblk_f0, kblk_f1, cf, hf);
         col_interval_of_block(n, qh, kh, kblk_l0, kblk_l1, cl, hl);
@@ -554,6 +556,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // dQ: query-stationary.
 // ---------------------------------------------------------------------------
+// 4 waves at every width (at D = 192, 8 waves sharing the K / V tiles would
+// need more than the 256 registers of two waves per SIMD).
 template <int D>
 struct DqCfg {
   static constexpr int NW = 4;
@@ -569,7 +573,7 @@ struct DqCfg {
 
 // SC: softcapping on (P from the capped scores, dS times 1 - tanh^2).
 template <int D, bool SC>
-__global__ __launch_bounds__(256, (D < 256 ? 2 : 1)) void bwd_dq_kernel(AttnArgs a, int qtiles) {
+__global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel(AttnArgs a, int qtiles) {
   using C = DqCfg<D>;
   using Tile = typename C::Tile;
   constexpr int BN = C::BN;
@@ -838,7 +842,9 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
 constexpr long long kDkdvMinBlocks = 1024;
 
 int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
-  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV, "one key tile size for D = 64 and 128");
+  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV && DkdvCfg<96>::BKV == DkdvCfg<128>::BKV &&
+                    DkdvCfg<192>::BKV == DkdvCfg<128>::BKV,
+                "one key tile size below D = 256");
   const int bkv = D == 256 ? DkdvCfg<256>::BKV : DkdvCfg<128>::BKV;
   const long long ktiles = ((long long)n + bkv - 1) / bkv;
   const long long base = ktiles * nhalves * B * Hkv;
@@ -853,6 +859,8 @@ int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
 
 hipError_t launch_bwd_stage(const AttnArgs& a, int D, int stage, hipStream_t s) {
   if (D == 64) return launch_stage_t<64>(a, stage, s);
+  if (D == 96) return launch_stage_t<96>(a, stage, s);
+  if (D == 192) return launch_stage_t<192>(a, stage, s);
   if (D == 256) return launch_stage_t<256>(a, stage, s);
   return launch_stage_t<128>(a, stage, s);
 }

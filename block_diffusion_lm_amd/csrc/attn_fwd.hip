@@ -60,8 +60,11 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // SC: softcapping on (the scores are capped before the mask and the
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
-// D = 256 holds Q and O in one wave's full register file (occupancy 1).
-__global__ __launch_bounds__(64 * NW, (NW == 4 && D < 256 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
+// D = 192 and 256: the double-buffered K / V tiles fill most of a CU's LDS,
+// so one workgroup per CU.  At D = 256 Q and O fill one wave's whole
+// register file (one wave per SIMD); at D = 192 they fit half of it, and 8
+// waves (256 query rows) share the tiles.
+__global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
@@ -321,6 +324,8 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
   if (D == 64) return launch_fwd_t<64, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  if (D == 96) return launch_fwd_t<96, 64, 4, 2>(a, s);
+  if (D == 192) return launch_fwd_t<192, 64, 8, 2>(a, s);
   if (D == 256) return launch_fwd_t<256, 64, 4, 2>(a, s);
   return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }

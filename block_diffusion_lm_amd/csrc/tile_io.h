@@ -21,11 +21,25 @@
 
 namespace bd {
 
+//
+// The right permutation depends on where a row starts among the banks.  A
+// row of D bf16 is D / 2 dwords:
+//  * D = 128, 256 (a multiple of 64 dwords): every row starts on bank 0, so
+//    16 consecutive rows need 16 distinct chunk positions: a permutation of
+//    0..15 (the 4-row groups of a transposing read land on distinct
+//    quarters of the banks through the high two bits);
+//  * D = 64, 192 (32 mod 64 dwords): odd rows start half-way along the
+//    banks, so 3 bits suffice, and they keep every chunk inside its
+//    aligned group of 8 (D = 192 rows hold 24 chunks);
+//  * D = 96 (48 mod 64 dwords): the 4 rows of a transposing read already
+//    start on 4 distinct quarters of the banks; rows 4 apart share a
+//    quarter and are separated by a 2-bit permutation, which keeps every
+//    chunk inside its aligned group of 4 (rows of 12 chunks).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  // D >= 128: rows of 16 or 32 chunks; the permutation of 0..15 keeps both
-  // read patterns on distinct banks (D = 256 rows span two bank lines).
-  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dimension");
+  if constexpr (D == 128 || D == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if constexpr (D == 96) return (row >> 2) & 3;
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

@@ -26,9 +26,9 @@
  *    Materialization, section 4.5: the statistic saved for the backward).
  *  - scale multiplies q.k before the softmax (callers usually pass
  *    1/sqrt(D)).  It must be finite and nonzero.
- *  - D must be 64, 128 or 256 (the FP8 forward: 64 or 128).  B, n (or S),
- *    H >= 1.  block_size >= 1; a block
- *    longer than a half is allowed (one block per half).  One sample's
+ *  - D must be 64, 96, 128, 192 or 256 (the FP8 forward: 64 or 128).
+ *    B, n (or S), H >= 1.  block_size >= 1; a block longer than a half is
+ *    allowed (one block per half).  One sample's
  *    tensor (2n or S tokens x H x D bf16) must be smaller than 2 GiB
  *    (BDATTN_ERR_UNSUPPORTED otherwise).
  *  - stream is a hipStream_t (NULL: the default stream).  Every call is
@@ -54,7 +54,7 @@ extern "C" {
 enum {
   BDATTN_OK = 0,
   BDATTN_ERR_INVALID = 1,      /* null pointer, misaligned pointer, bad size or scale */
-  BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64, 128 or 256 */
+  BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64, 96, 128, 192 or 256 */
   BDATTN_ERR_LAUNCH = 3,       /* the HIP runtime refused a launch */
 };
 
@@ -193,7 +193,7 @@ int causal_attn_bwd_gqa(const void* q, const void* k, const void* v, const void*
  * Grouped heads as in the _gqa entry points.  Same pointer, size and
  * error rules as diffusion_attn_fwd, plus: the descale arrays must be
  * non-NULL and 4-byte aligned, and D must be 64 or 128
- * (BDATTN_ERR_UNSUPPORTED for 256).  There is no FP8 backward.
+ * (BDATTN_ERR_UNSUPPORTED for 96, 192 and 256).  There is no FP8 backward.
  */
 int diffusion_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                            const float* k_descale, const float* v_descale, void* out, float* lse,

@@ -55,7 +55,7 @@ def _fwd(**kw):
     (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(v=FAKE + 2), INVALID),
     (dict(B=0), INVALID), (dict(n=0), INVALID), (dict(H=-1), INVALID), (dict(b=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=0.0), INVALID),
-    (dict(n=2 ** 30 + 1), INVALID), (dict(D=96), UNSUPPORTED), (dict(D=512), UNSUPPORTED),
+    (dict(n=2 ** 30 + 1), INVALID), (dict(D=80), UNSUPPORTED), (dict(D=512), UNSUPPORTED),
     (dict(n=2 ** 22, H=2, D=128), UNSUPPORTED),
     # 2^31 rows in all (over the 32-bit row limit), each sample small
     (dict(B=2 ** 20, n=1024, H=1, D=64), INVALID),
@@ -127,7 +127,7 @@ def test_grouped_entry_points_reject_bad_kv_heads(H, H_kv):
 
 def test_grouped_entry_points_share_the_other_checks():
     lib = bd.lib()
-    assert lib.diffusion_attn_fwd_gqa(*([FAKE] * 5), 1, 16, 4, 2, 96, 4, 0.125, None) == UNSUPPORTED
+    assert lib.diffusion_attn_fwd_gqa(*([FAKE] * 5), 1, 16, 4, 2, 160, 4, 0.125, None) == UNSUPPORTED
     assert lib.diffusion_attn_fwd_gqa(None, *([FAKE] * 4), 1, 16, 4, 2, 64, 4, 0.125, None) == INVALID
     assert lib.diffusion_attn_bwd_gqa(*([FAKE] * 9), 1, 16, 4, 2, 64, 4, 0.125, FAKE, 4, None) == INVALID
 
@@ -164,6 +164,8 @@ def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     (3, 5000, 12, 12, 64),   # plain multi-head
     (2, 4096, 16, 2, 256),   # 512 workgroups of 64 keys: S = 2
     (1, 1000, 8, 1, 256),
+    (2, 4096, 16, 2, 192),   # 512 workgroups of 128 keys: S = 2
+    (2, 900, 12, 3, 96),
 ])
 def test_gqa_workspace_sizes(B, n, H, Hkv, D):
     want, S = _expected_gqa_workspace(B, n, H, Hkv, D)
@@ -197,7 +199,7 @@ def test_varlen_rejects_bad_arguments():
     assert fwd(FAKE, 2, 16, -1, 4, 2, 64, 4) == INVALID    # negative total
     assert fwd(FAKE, 0, 16, 40, 4, 2, 64, 4) == INVALID    # no samples
     assert fwd(FAKE, 2, 16, 40, 4, 3, 64, 4) == INVALID    # H not a multiple of H_kv
-    assert fwd(FAKE, 2, 16, 40, 4, 2, 96, 4) == UNSUPPORTED
+    assert fwd(FAKE, 2, 16, 40, 4, 2, 160, 4) == UNSUPPORTED
     # all rows past the 32-bit row limit
     assert fwd(FAKE, 2, 16, 2 ** 30, 4, 2, 64, 4) == INVALID
     bwd = lambda cu, wsb, *a: lib.diffusion_attn_varlen_bwd(*([FAKE] * 9), cu, *a, 0.125, FAKE, wsb, None)
@@ -242,8 +244,9 @@ def test_fp8_forward_rejects_bad_arguments():
         FAKE, FAKE, FAKE, qd, kd, vd, FAKE, FAKE, 1, 16, 4, H_kv, D, 4, 0.125, None)
     assert f(qd=None) == INVALID and f(kd=None) == INVALID and f(vd=None) == INVALID
     assert f(vd=FAKE + 2) == INVALID            # descales must be 4-byte aligned
-    assert f(D=96) == UNSUPPORTED
-    assert f(D=256) == UNSUPPORTED              # no FP8 kernel at D = 256
+    assert f(D=80) == UNSUPPORTED
+    for D in (96, 192, 256):                    # no FP8 kernel at these widths
+        assert f(D=D) == UNSUPPORTED
     assert f(H_kv=3) == INVALID
     assert lib.causal_attn_fwd_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 4, 64, 0.1,
                                    None) == INVALID

@@ -166,10 +166,13 @@ def test_smallest_workload():
     compare_full(res, q, k, v, do, w.b, scale, "c1")
 
 
+# every head dimension of the bf16 kernels
+HEAD_DIMS = [64, 96, 128, 192, 256]
+
 EDGE = [(n, b) for n in (1, 7, 100, 129, 300) for b in (1, 3, 16, 64, 127, 200, n, n + 5)]
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 @pytest.mark.parametrize("n,b", EDGE)
 def test_edge_shapes(n, b, D):
     """Ragged halves (n not a multiple of any tile), blocks of 1 token, blocks
@@ -180,7 +183,7 @@ def test_edge_shapes(n, b, D):
     compare_full(res, q, k, v, do, b, scale, f"n{n} b{b} D{D}")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 @pytest.mark.parametrize("S", [1, 7, 129, 300])
 def test_causal_small(S, D):
     q, k, v, do = make_inputs(3, S, 2, D, seed=8000 + S + D)
@@ -201,7 +204,7 @@ def test_scale_other_than_default():
     compare_full(res, q, k, v, do, 5, 0.3, "scale 0.3")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_negative_scale(D):
     # the forward folds the sign into Q; the backward uses the signed factor
     q, k, v, do = make_inputs(1, 150, 2, D, seed=9002)
@@ -231,7 +234,7 @@ def test_bitwise_reproducible():
         assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_block_size_one_clean_half_equals_causal_bitwise(D):
     """With block size 1 the clean half is causal attention on the clean
     tokens (Fast Diffusion Attention, "Accuracy"); both entry points run the
@@ -318,13 +321,15 @@ def test_block_size_sweep(name):
     compare_full(res, q, k, v, do, w.b, scale, name, heads=[(3, 7)])
 
 
-def test_head_dim_256_workload():
-    """Head dimension 256 at full size: every output of two heads."""
-    w = HEAD_DIM_WORKLOADS["h1"]
+@pytest.mark.parametrize("name", sorted(HEAD_DIM_WORKLOADS))
+def test_head_dim_workload(name):
+    """Head dimensions 96, 192 and 256 at full size: every output of two
+    heads."""
+    w = HEAD_DIM_WORKLOADS[name]
     q, k, v, do = make_workload_inputs(w)
     scale = 1 / math.sqrt(w.D)
     res = run_diffusion(q, k, v, do, w.b, scale)
-    compare_full(res, q, k, v, do, w.b, scale, "h1", heads=[(0, 0), (3, 7)])
+    compare_full(res, q, k, v, do, w.b, scale, name, heads=[(0, 0), (w.B - 1, w.H - 1)])
 
 
 def _sample_positions(n, b, rng, count):
@@ -415,6 +420,7 @@ GQA_SMALL = [  # B, n, H, H_kv, D, b
     (2, 100, 4, 2, 64, 16), (1, 129, 6, 3, 128, 7), (2, 300, 4, 1, 64, 64),
     (1, 7, 8, 2, 128, 3), (1, 257, 8, 1, 128, 32), (2, 64, 3, 1, 64, 200),
     (1, 200, 4, 1, 256, 16), (2, 65, 6, 2, 256, 5),
+    (2, 150, 8, 2, 96, 12), (1, 333, 6, 1, 192, 40),
 ]
 
 
@@ -426,7 +432,7 @@ def test_grouped_small(B, n, H, Hkv, D, b):
     compare_grouped(res, q, k, v, do, b, scale, f"gqa n{n} H{H}/{Hkv} D{D} b{b}")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_grouped_causal_small(D):
     q, k, v, do = make_inputs(2, 150, 6, D, seed=9400 + D, H_kv=2)
     q, k, v, do = (x[:, :150].contiguous() for x in (q, k, v, do))
@@ -435,7 +441,7 @@ def test_grouped_causal_small(D):
     compare_grouped(res, q, k, v, do, 1, scale, f"causal gqa D{D}", causal=True)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_grouped_matches_repeated_heads(D):
     """Each query head reads its group's key/value head, so O, LSE and dQ
     equal (bit for bit) the plain entry points on key/value heads repeated
@@ -553,6 +559,8 @@ VARLEN_SMALL = [  # half lengths, H, H_kv, D, b
     ([1, 2, 3, 200], 6, 1, 64, 200),
     ([128, 384, 127, 129], 2, 2, 128, 32),
     ([100, 0, 65, 257], 2, 1, 256, 16),
+    ([33, 0, 190, 64], 4, 2, 96, 8),
+    ([129, 5, 0, 260], 2, 2, 192, 48),
 ]
 
 
@@ -573,7 +581,7 @@ def test_varlen_small(ns, H, Hkv, D, b):
         check_grad(res[name], ref, name, tag)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_varlen_equals_batched_per_sample_bitwise(D):
     """Each packed sample is computed exactly as the batched entry points
     compute it alone (Fast Diffusion Attention, "Accuracy": the varlen
@@ -871,6 +879,7 @@ SOFTCAP_SHAPES = [  # B, n, H, H_kv, D, b, cap
     (2, 100, 2, 2, 64, 16, 5.0), (1, 129, 4, 2, 128, 7, 1.0), (2, 300, 4, 1, 64, 64, 2.5),
     (1, 64, 2, 2, 128, 200, 0.5), (1, 257, 8, 2, 128, 32, 20.0),
     (1, 130, 4, 2, 256, 9, 3.0),
+    (1, 140, 4, 4, 96, 6, 4.0), (2, 97, 2, 1, 192, 33, 2.0),
 ]
 
 
@@ -893,7 +902,7 @@ def test_softcap_small(B, n, H, Hkv, D, b, cap):
         check_grad(res[name], ref, name, tag)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", HEAD_DIMS)
 def test_softcap_causal_and_varlen(D):
     cap, scale = 2.0, -0.3  # a negative scale too: the cap keeps its sign
     q, k, v, do = make_inputs(2, 150, 2, D, seed=10200 + D)

@@ -70,11 +70,13 @@ for _D in (64, 128):
         _w = _c5(_D, _b)
         WORKLOADS[_w.name] = _w
 
-# Head dimension 256: the block-size-sweep problem with half the heads at
-# twice the width (the same tokens, bytes and FLOPs as its D = 128, b = 48
-# member).
+# Head dimensions other than 64 and 128, on the block-size-sweep problem
+# (n = 4096, b = 48): at D = 256 with half the heads (the same tokens, bytes
+# and FLOPs as its D = 128 member); at D = 192 and D = 96 with its 16 heads.
 HEAD_DIM_WORKLOADS: Dict[str, Workload] = {
     "h1": Workload("h1", B=4, n=4096, H=8, D=256, b=48, seed=1031),
+    "h2": Workload("h2", B=4, n=4096, H=16, D=192, b=48, seed=1032),
+    "h3": Workload("h3", B=4, n=4096, H=16, D=96, b=48, seed=1033),
 }
 
 # Grouped-query problems (query heads sharing key/value heads): the
