@@ -441,9 +441,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the attention of every (sample, head) is independent; see the design notes "
-              "for how it would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path (the attention "
+              "of every (sample, head) is independent, so batch or head shards would need no "
+              "communication inside attention).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -22,7 +22,7 @@ Sources (cited by page title and section):
   dV = P^T dO, dP = dO V^T, delta_i = sum_j P_ij dP_ij,
   dS = P * (dP - delta), dQ = scale * dS K, dK = scale * dS^T Q.
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
 
 * Blocks are consecutive runs of b tokens from the start of each half; the
   last block of a half is shorter when b does not divide n.  Block

@@ -3,8 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Fast Diffusion Attention, "Results" (the FP8 forward pass) names the
-operation but not its quantisation; the readings taken here (each listed
-in the design notes):
+operation but not its quantisation; the readings taken here:
 
 * q, k and v arrive as OCP FP8 E4M3 values (1 sign bit, 4 exponent bits
   with bias 7, 3 mantissa bits; no infinities, one NaN pattern per sign,
