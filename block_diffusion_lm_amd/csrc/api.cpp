@@ -399,6 +399,7 @@ int bdattn_bwd_stage(int mode, int stage, const void* q, const void* k, const vo
                      size_t workspace_bytes_, void* stream) {
   if (mode != bd::MODE_DIFFUSION && mode != bd::MODE_CAUSAL) return BDATTN_ERR_INVALID;
   if (stage < 0 || stage > 1) return BDATTN_ERR_INVALID;
+  if (cu_seqlens && total_tokens == 0) return BDATTN_OK;
   return run_bwd(general(mode, cu_seqlens, B, n, total_tokens, H, H_kv, D, block_size, scale, softcap),
                  stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
 }

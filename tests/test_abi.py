@@ -260,8 +260,12 @@ def test_general_entry_points_check_softcap_and_mode():
     assert fwd(mode=2) == INVALID
     bwd = lambda cap: lib.bdattn_bwd(0, *([FAKE] * 9), None, 1, 16, 0, 2, 2, 64, 4, 0.125, cap, FAKE, 1 << 20, None)
     assert bwd(-0.5) == INVALID
-    # packed with no tokens: nothing to do
+    # packed with no tokens: nothing to do, in every packed entry point
     assert lib.bdattn_fwd(0, *([FAKE] * 5), FAKE, 3, 0, 0, 2, 2, 64, 4, 0.125, 1.0, None) == OK
+    assert lib.bdattn_bwd(0, *([FAKE] * 9), FAKE, 3, 0, 0, 2, 2, 64, 4, 0.125, 1.0, FAKE, 0, None) == OK
+    for stage in (0, 1):
+        assert lib.bdattn_bwd_stage(0, stage, *([FAKE] * 9), FAKE, 3, 0, 0, 2, 2, 64, 4, 0.125, 1.0,
+                                    FAKE, 0, None) == OK
 
 
 def test_general_workspace_size_matches_the_specific_ones():
