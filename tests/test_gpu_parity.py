@@ -986,3 +986,64 @@ def test_split_groups_and_varlen_are_bitwise_reproducible():
     b = run_varlen(pq, pk, pv, pdo, cu, max(ns), 16, 0.125)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# Randomised combinations of every option, compared in full
+# ---------------------------------------------------------------------------
+
+def _random_case(i):
+    """The i-th of a fixed list of small problems: mode, batched or packed
+    layout, head grouping, head dimension, block size (tile-aligned or not,
+    longer than a half), softcap and the sign and size of the scale, drawn
+    from a generator seeded with i."""
+    r = np.random.default_rng(20250 + i)
+    mode = bd.MODE_CAUSAL if r.random() < 0.3 else bd.MODE_DIFFUSION
+    packed = r.random() < 0.4
+    D = int(r.choice(HEAD_DIMS))
+    Hkv = int(r.integers(1, 4))
+    H = Hkv * int(r.choice([1, 1, 2, 3, 4]))
+    if packed:
+        ns = [int(x) for x in r.integers(0, 260, size=int(r.integers(1, 5)))]
+        if max(ns) == 0:
+            ns[0] = 1  # at least one non-empty sample
+        n = max(ns)
+    else:
+        ns = None
+        n = int(r.integers(1, 300))
+    b = int(r.choice([1, 2, 3, 4, 5, 8, 16, 31, 32, 33, 48, 64, 100, n + 3]))
+    cap = float(r.choice([0.0, 0.0, 0.0, 1.5, 6.0]))
+    scale = float(r.choice([1.0, 1.0, -1.0, 0.5, 2.0])) / math.sqrt(D)
+    B = 1 if packed else int(r.integers(1, 4))
+    return dict(mode=mode, packed=packed, D=D, H=H, Hkv=Hkv, ns=ns, n=n, b=b, cap=cap, scale=scale, B=B)
+
+
+@pytest.mark.parametrize("i", range(96))
+def test_random_configurations(i):
+    c = _random_case(i)
+    f = oracle.to_f64
+    causal = c["mode"] == bd.MODE_CAUSAL
+    b = 1 if causal else c["b"]
+    tag = (f"case {i}: {'causal' if causal else 'diffusion'} {'packed ' + str(c['ns']) if c['packed'] else 'B=' + str(c['B']) + ' n=' + str(c['n'])}"
+           f" H{c['H']}/{c['Hkv']} D{c['D']} b{b} cap {c['cap']} scale {c['scale']:.3g}")
+    print(tag, flush=True)
+    kw = dict(scale=c["scale"], softcap=c["cap"])
+    if not causal:
+        kw["b"] = b
+    fn_f = oracle.causal_forward if causal else oracle.diffusion_forward
+    fn_b = oracle.causal_backward if causal else oracle.diffusion_backward
+    if c["packed"]:
+        q, k, v, do, cu = make_varlen_inputs(c["ns"], c["H"], c["D"], seed=30000 + i, H_kv=c["Hkv"], causal=causal)
+        res = run_general(c["mode"], q, k, v, do, b, c["scale"], c["cap"], cu=cu, max_n=c["n"])
+        O, L = oracle.varlen_forward(fn_f, f(q), f(k), f(v), cu, **kw)
+        G = oracle.varlen_backward(fn_b, f(q), f(k), f(v), f(do), cu, **kw)
+    else:
+        q, k, v, do = make_inputs(c["B"], c["n"], c["H"], c["D"], seed=30000 + i, H_kv=c["Hkv"])
+        if causal:
+            q, k, v, do = (make_causal_view(x) for x in (q, k, v, do))
+        res = run_general(c["mode"], q, k, v, do, b, c["scale"], c["cap"])
+        O, L = oracle.grouped_forward(fn_f, f(q), f(k), f(v), **kw)
+        G = oracle.grouped_backward(fn_b, f(q), f(k), f(v), f(do), **kw)
+    check_fwd(res["out"], res["lse"], O, L, tag)
+    for name, ref in zip(("dq", "dk", "dv"), G):
+        check_grad(res[name], ref, name, tag)
