@@ -1018,6 +1018,25 @@ def _random_case(i):
     return dict(mode=mode, packed=packed, D=D, H=H, Hkv=Hkv, ns=ns, n=n, b=b, cap=cap, scale=scale, B=B)
 
 
+def check_fwd_rounding(o, lse, o_ref, lse_ref, pv_ref, what):
+    """Forward check for scales other than the workloads' 1/sqrt(D): an
+    element is held to 1e-2, or, where that is exceeded, to what rounding
+    can cost it: half a bf16 ulp of the output plus the bf16 rounding of the
+    probabilities fed to P.V, at most 2^-9 sum_j P_ij |v_j| (taken as 2^-8,
+    with 1e-3 for the float32 accumulation).  pv_ref is the oracle's
+    sum_j P_ij |v_j| (its forward on |v|).  LSE as in check_fwd."""
+    o = oracle.to_f64(o)
+    err = np.abs(o - o_ref)
+    bound = np.maximum(FWD_TOL, _halfulp_bf16(o_ref) + 2.0 ** -8 * pv_ref + 1e-3)
+    worst = np.argmax(err - bound)
+    assert np.all(err <= bound), (f"{what}: forward error {err.flat[worst]:.3g} > bound {bound.flat[worst]:.3g} "
+                                  f"(|O_ref| {abs(o_ref.flat[worst]):.3g}, P|V| {pv_ref.flat[worst]:.3g})")
+    lerr = np.abs(oracle.to_f64(lse) - lse_ref).max()
+    assert lerr <= LSE_TOL, f"{what}: LSE max-abs error {lerr:.3g} > {LSE_TOL}"
+    print(f"[{what}] fwd max err {err.max():.3g} (elements past 1e-2: {int((err > FWD_TOL).sum())}), "
+          f"lse err {lerr:.3g}")
+
+
 @pytest.mark.parametrize("i", range(96))
 def test_random_configurations(i):
     c = _random_case(i)
@@ -1036,6 +1055,7 @@ def test_random_configurations(i):
         q, k, v, do, cu = make_varlen_inputs(c["ns"], c["H"], c["D"], seed=30000 + i, H_kv=c["Hkv"], causal=causal)
         res = run_general(c["mode"], q, k, v, do, b, c["scale"], c["cap"], cu=cu, max_n=c["n"])
         O, L = oracle.varlen_forward(fn_f, f(q), f(k), f(v), cu, **kw)
+        PV, _ = oracle.varlen_forward(fn_f, f(q), f(k), np.abs(f(v)), cu, **kw)
         G = oracle.varlen_backward(fn_b, f(q), f(k), f(v), f(do), cu, **kw)
     else:
         q, k, v, do = make_inputs(c["B"], c["n"], c["H"], c["D"], seed=30000 + i, H_kv=c["Hkv"])
@@ -1043,7 +1063,11 @@ def test_random_configurations(i):
             q, k, v, do = (make_causal_view(x) for x in (q, k, v, do))
         res = run_general(c["mode"], q, k, v, do, b, c["scale"], c["cap"])
         O, L = oracle.grouped_forward(fn_f, f(q), f(k), f(v), **kw)
+        PV, _ = oracle.grouped_forward(fn_f, f(q), f(k), np.abs(f(v)), **kw)
         G = oracle.grouped_backward(fn_b, f(q), f(k), f(v), f(do), **kw)
-    check_fwd(res["out"], res["lse"], O, L, tag)
+    if c["scale"] * math.sqrt(c["D"]) == 1.0:
+        check_fwd(res["out"], res["lse"], O, L, tag)
+    else:
+        check_fwd_rounding(res["out"], res["lse"], O, L, PV, tag)
     for name, ref in zip(("dq", "dk", "dv"), G):
         check_grad(res[name], ref, name, tag)
