@@ -50,8 +50,12 @@ def visible_pairs(n: int, b: int) -> int:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 35 steps of the default workload take about 330 ms: the warm-up and the
+    # timed region each last at least 300 ms, so that a power-capped clock has
+    # settled before timing (Fast Diffusion Attention, "Measuring on
+    # power-capped GPUs")
+    ap.add_argument("--steps", type=int, default=35)
+    ap.add_argument("--warmup", type=int, default=35)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--rounds", type=int, default=5, help="interleaved diffusion/causal rounds")
     ap.add_argument("--round-ms", type=float, default=300.0, help="target duration of each phase of a round")
