@@ -60,11 +60,11 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // SC: softcapping on (the scores are capped before the mask and the
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
-// D = 192 and 256: the double-buffered K / V tiles fill most of a CU's LDS,
-// so one workgroup per CU.  At D = 256 Q and O fill one wave's whole
-// register file (one wave per SIMD); at D = 192 they fit half of it, and 8
-// waves (256 query rows) share the tiles.
-__global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
+// D = 192: the double-buffered 64-key K / V tiles fill most of a CU's LDS,
+// so one workgroup per CU, and 8 waves (256 query rows) share them, two per
+// SIMD.  D = 256: 32-key tiles, two workgroups per CU (Q and O take most of
+// half a register file).
+__global__ __launch_bounds__(64 * NW, (NW == 4 && (D < 192 || BN == 32) ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
@@ -148,6 +148,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_ker
   row_interval(g, qh, seg.half1, pw0, lo_f1, hi_f1);
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);
+  // The blocks of the wave's first and last rows and of this lane's row.
+  // At D >= 192 the intervals of a tile's half are derived from these per
+  // tile: selected from the two halves' copies, they ended up read through
+  // a table of addresses in scratch memory.
+  const int bs_f = g.bstart(pw0), be_f = g.bend(pw0);
+  const int bs_l = g.bstart(max(pw1 - 1, pw0)), be_l = g.bend(max(pw1 - 1, pw0));
+  const int bs_p = g.bstart(p), be_p = g.bend(p);
   const size_t kvb0 = (sample0 + half_offset(a, seg.half0, n)) * rs_kv + (size_t)hk * D;
   const size_t kvb1 = (sample0 + half_offset(a, seg.half1, n)) * rs_kv + (size_t)hk * D;
 
@@ -166,15 +173,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_ker
   float m_run = -INFINITY;  // running maximum, base-2 units, scale applied
   float l_run = 0.f;        // this lane's share of the denominator
 
-  // Per-lane parts of the LDS addresses, fixed for the whole walk.
-  int koff[C::KS];
+  // Per-lane parts of the LDS addresses, fixed for the whole walk: one
+  // entry per chunk position within the swizzle's span (k-step s reads
+  // chunk 2s + h2, column block db chunks 4db ..); the span-multiples are
+  // compile-time offsets.
+  constexpr int KP = swz_span<D>() / 2 < C::KS ? swz_span<D>() / 2 : C::KS;
+  constexpr int DP = swz_span<D>() / 4 < C::DB ? swz_span<D>() / 4 : C::DB;
+  int koff_[KP];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) koff[s] = row8_lane_off<D>(lane, 2 * s);
-  int voff[C::DB][2];
+  for (int s = 0; s < KP; ++s) koff_[s] = row8_lane_off<D>(lane, 2 * s);
+  int voff_[DP][2];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < DP; ++db)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) voff[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+    for (int u = 0; u < 2; ++u) voff_[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+  auto koff = [&](int s) __attribute__((always_inline)) { return koff_[s % KP] + (s / KP) * (16 * KP); };
+  auto voff = [&](int db, int u) __attribute__((always_inline)) { return voff_[db % DP][u] + (db / DP) * (32 * DP); };
 
   // Prologue: the first NBUF - 1 tiles in flight, the first one landed.
 #pragma unroll
@@ -196,9 +210,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_ker
     if (wave_active) {
       const bool second = i >= n0;
       const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
-      const int lf = second ? lo_f1 : lo_f0, hf = second ? hi_f1 : hi_f0;
-      const int ll = second ? lo_l1 : lo_l0, hl = second ? hi_l1 : hi_l0;
-      const int lo = second ? lo_p1 : lo_p0, hi = second ? hi_p1 : hi_p0;
+      int lf, hf, ll, hl, lo, hi;
+      if constexpr (D >= 192) {
+        const int kh = second ? seg.half1 : seg.half0;
+        row_interval_of_block(qh, kh, bs_f, be_f, lf, hf);
+        row_interval_of_block(qh, kh, bs_l, be_l, ll, hl);
+        row_interval_of_block(qh, kh, bs_p, be_p, lo, hi);
+      } else {
+        lf = second ? lo_f1 : lo_f0;
+        hf = second ? hi_f1 : hi_f0;
+        ll = second ? lo_l1 : lo_l0;
+        hl = second ? hi_l1 : hi_l0;
+        lo = second ? lo_p1 : lo_p0;
+        hi = second ? hi_p1 : hi_p0;
+      }
       int cls[C::KB];
       floatx16 sc[C::KB];
       float mt = -INFINITY;
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_ker
         floatx16 acc = zero16();
         mfma_burst_begin();
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_vec_at(Ks + 32 * kb * D + koff[s]), qf[s], acc);
+        for (int s = 0; s < C::KS; ++s) acc = mfma32(lds_vec_at(Ks + 32 * kb * D + koff(s)), qf[s], acc);
         mfma_burst_end();
         if constexpr (SC) {
 #pragma unroll
@@ -261,7 +286,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && D < 192 ? 2 : 1)) void fwd_ker
           const uint16_t* vrow = Vs + (32 * kb + 16 * ks) * D;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            o[db] = mfma32(lds_trA_at(vrow + voff[db][0], vrow + voff[db][1]), ks ? pb1 : pb0, o[db]);
+            o[db] = mfma32(lds_trA_at(vrow + voff(db, 0), vrow + voff(db, 1)), ks ? pb1 : pb0, o[db]);
         }
         mfma_burst_end();
       }
@@ -326,7 +351,7 @@ hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
   if (D == 64) return launch_fwd_t<64, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
   if (D == 96) return launch_fwd_t<96, 64, 4, 2>(a, s);
   if (D == 192) return launch_fwd_t<192, 64, 8, 2>(a, s);
-  if (D == 256) return launch_fwd_t<256, 64, 4, 2>(a, s);
+  if (D == 256) return launch_fwd_t<256, 32, 4, 2>(a, s);
   return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }
 

@@ -47,7 +47,19 @@ struct Geom {
   }
 };
 
-// Visible keys of query row p (half qh) inside key half kh: [lo, hi).
+// Visible keys inside key half kh of a query row of half qh whose block is
+// [bs, be): [lo, hi).
+BD_HD void row_interval_of_block(int qh, int kh, int bs, int be, int& lo, int& hi) {
+  lo = (qh == NOISY && kh == NOISY) ? bs : 0;  // own noisy block, both directions
+  hi = (qh == NOISY) ? (kh == NOISY ? be       // ... up to the end of the block
+                                    : bs)      // clean blocks strictly before own block
+                     : (kh == CLEAN ? be       // clean blocks up to and including own block
+                                    : 0);      // clean rows see no noisy key
+}
+
+// Visible keys of query row p (half qh) inside key half kh: [lo, hi); the
+// same as row_interval_of_block with p's block (tests/test_geometry_header.py
+// checks this exhaustively on small shapes).
 BD_HD void row_interval(const Geom& g, int qh, int kh, int p, int& lo, int& hi) {
   if (qh == NOISY && kh == NOISY) {        // own noisy block, both directions
     lo = g.bstart(p);

@@ -43,6 +43,16 @@ __device__ __forceinline__ int swz(int row) {
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
+// The chunks swz permutes: chunk c ^ swz(r) stays in c's aligned group of
+// this many chunks, so chunks SPAN apart sit SPAN * 8 elements apart in
+// every row.  Per-lane offset tables therefore need one entry per position
+// in the group; the rest is a compile-time offset (an immediate of the LDS
+// instruction).
+template <int D>
+constexpr int swz_span() {
+  return D == 96 ? 4 : (D == 128 || D == 256) ? 16 : 8;
+}
+
 template <int D>
 __device__ __forceinline__ int nat_off(int row, int chunk) {
   return row * D + ((chunk ^ swz<D>(row)) << 3);
