@@ -60,10 +60,8 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // SC: softcapping on (the scores are capped before the mask and the
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
-// D = 192: the double-buffered 64-key K / V tiles fill most of a CU's LDS,
-// so one workgroup per CU, and 8 waves (256 query rows) share them, two per
-// SIMD.  D = 256: 32-key tiles, two workgroups per CU (Q and O take most of
-// half a register file).
+// D = 192 and 256: 32-key K / V tiles, so that two workgroups fit a CU's
+// LDS (Q and O take most of half a register file).
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (D < 192 || BN == 32) ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
@@ -350,7 +348,7 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
   if (D == 64) return launch_fwd_t<64, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
   if (D == 96) return launch_fwd_t<96, 64, 4, 2>(a, s);
-  if (D == 192) return launch_fwd_t<192, 64, 8, 2>(a, s);
+  if (D == 192) return launch_fwd_t<192, 32, 4, 2>(a, s);
   if (D == 256) return launch_fwd_t<256, 32, 4, 2>(a, s);
   return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
 }
