@@ -67,6 +67,11 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
   const size_t sb1 = stat_base + half_off(a, seg.half1, n);
 
 #define ROW_SEGMENTS                                                           \
+  constexpr bool ROW_BLOCKS = D >= 192;  /* per-tile intervals from the rows' blocks */ \
+  const int bs_f = ROW_BLOCKS ? g.bstart(pw0) : 0, be_f = ROW_BLOCKS ? g.bend(pw0) : 0; \
+  const int bs_l = ROW_BLOCKS ? g.bstart(max(pw1 - 1, pw0)) : 0;               \
+  const int be_l = ROW_BLOCKS ? g.bend(max(pw1 - 1, pw0)) : 0;                 \
+  const int bs_p = ROW_BLOCKS ? g.bstart(p) : 0, be_p = ROW_BLOCKS ? g.bend(p) : 0; \
   int lo_f0, hi_f0, lo_l0, hi_l0, lo_p0, hi_p0, lo_f1, hi_f1, lo_l1, hi_l1, lo_p1, hi_p1; \
   row_interval(g, qh, seg.half0, pw0, lo_f0, hi_f0);                            \
   row_interval(g, qh, seg.half0, max(pw1 - 1, pw0), lo_l0, hi_l0);              \
@@ -686,14 +691,20 @@ __global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel
 
   // Per-lane LDS offsets (elements from the start of a buffer): natural rows
   // of K and V (S^T = K Q^T, dP^T = V dO^T) and transposed K (dQ^T).
-  int roff[C::KS];
+  // One entry per chunk position within the swizzle's span; the
+  // span-multiples are compile-time offsets.
+  constexpr int KP = swz_span<D>() / 2 < C::KS ? swz_span<D>() / 2 : C::KS;
+  constexpr int DP = swz_span<D>() / 4 < C::DB ? swz_span<D>() / 4 : C::DB;
+  int roff_[KP];
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) roff[s] = row8_lane_off<D>(lane, 2 * s);
-  int toff[C::DB][2];
+  for (int s = 0; s < KP; ++s) roff_[s] = row8_lane_off<D>(lane, 2 * s);
+  int toff_[DP][2];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < DP; ++db)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) toff[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+    for (int u = 0; u < 2; ++u) toff_[db][u] = trA_lane_off<D>(lane, 32 * db, u);
+  auto roff = [&](int s) __attribute__((always_inline)) { return roff_[s % KP] + (s / KP) * (16 * KP); };
+  auto toff = [&](int db, int u) __attribute__((always_inline)) { return toff_[db % DP][u] + (db / DP) * (32 * DP); };
 
   if (ntiles > 0) issue_tile(0, 0);
   wait_vmem();
@@ -710,9 +721,23 @@ __global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel
     if (wave_active) {
       const bool second = i >= n0;
       const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
-      const int lf = second ? lo_f1 : lo_f0, hf = second ? hi_f1 : hi_f0;
-      const int ll = second ? lo_l1 : lo_l0, hl = second ? hi_l1 : hi_l0;
-      const int lo = second ? lo_p1 : lo_p0, hi = second ? hi_p1 : hi_p0;
+      // At D >= 192 the intervals of the tile's half are derived from the
+      // rows' blocks: selected from the two halves' copies, they ended up
+      // read through a table of addresses in scratch memory.
+      int lf, hf, ll, hl, lo, hi;
+      if constexpr (ROW_BLOCKS) {
+        const int kh = second ? seg.half1 : seg.half0;
+        row_interval_of_block(qh, kh, bs_f, be_f, lf, hf);
+        row_interval_of_block(qh, kh, bs_l, be_l, ll, hl);
+        row_interval_of_block(qh, kh, bs_p, be_p, lo, hi);
+      } else {
+        lf = second ? lo_f1 : lo_f0;
+        hf = second ? hi_f1 : hi_f0;
+        ll = second ? lo_l1 : lo_l0;
+        hl = second ? hi_l1 : hi_l0;
+        lo = second ? lo_p1 : lo_p0;
+        hi = second ? hi_p1 : hi_p0;
+      }
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const int c0 = k0 + 32 * kb;
@@ -725,15 +750,15 @@ __global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel
         bf16x8 ak[C::KS], av[C::KS];
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
-          ak[s] = lds_vec_at(Ks + 32 * kb * D + roff[s]);
-          av[s] = lds_vec_at(Vs + 32 * kb * D + roff[s]);
+          ak[s] = lds_vec_at(Ks + 32 * kb * D + roff(s));
+          av[s] = lds_vec_at(Vs + 32 * kb * D + roff(s));
         }
         mfma_burst_begin();
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
           if (s + PF < C::KS) {
-            ak[s + PF] = lds_vec_at(Ks + 32 * kb * D + roff[s + PF]);
-            av[s + PF] = lds_vec_at(Vs + 32 * kb * D + roff[s + PF]);
+            ak[s + PF] = lds_vec_at(Ks + 32 * kb * D + roff(s + PF));
+            av[s + PF] = lds_vec_at(Vs + 32 * kb * D + roff(s + PF));
           }
           sp = mfma32(ak[s], qf[s], sp);
           dp = mfma32(av[s], gf[s], dp);
@@ -772,7 +797,7 @@ __global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel
           const uint16_t* kr = Ks + (32 * kb + 16 * ks) * D;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            dq[db] = mfma32(lds_trA_at(kr + toff[db][0], kr + toff[db][1]), ks ? sb1 : sb0, dq[db]);
+            dq[db] = mfma32(lds_trA_at(kr + toff(db, 0), kr + toff(db, 1)), ks ? sb1 : sb0, dq[db]);
         }
         mfma_burst_end();
       }
