@@ -97,13 +97,16 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
 // D = 192 and 256 stream 32-row query tiles, so that the three-deep Q / dO
 // ring fits LDS; D = 256 also runs two pairs only (one wave per SIMD, each
 // with the whole register file), while D = 192 still fits two waves per SIMD.
+// D = 64 streams 32-row tiles too: its LDS (42 KiB) and registers (at most
+// 128) then fit two workgroups per CU, four waves per SIMD.
 template <int D>
 struct DkdvCfg {
   static constexpr bool WIDE = D >= 192;
+  static constexpr int WGS = D == 64 ? 2 : 1;  // workgroups per CU
   static constexpr int NPAIR = D == 256 ? 2 : 4;
   static constexpr int NT = 128 * NPAIR;  // 8 waves (4 at D = 256)
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
-  static constexpr int BQ = WIDE ? 32 : 64;  // query rows per streamed tile
+  static constexpr int BQ = (WIDE || D == 64) ? 32 : 64;  // query rows per streamed tile
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -125,7 +128,7 @@ struct DkdvCfg {
 // P-wave recomputes P from the capped scores and publishes
 // P (1 - tanh^2), so that the dS-wave's dS carries the cap's derivative).
 template <int D, bool GROUPED, bool SC>
-__global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
+__global__ __launch_bounds__(DkdvCfg<D>::NT, DkdvCfg<D>::WGS) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
   using C = DkdvCfg<D>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NBUF * C::BUF];
@@ -269,12 +272,12 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT, 1) void bwd_dkdv_kernel(AttnArgs a,
       const int i = t - head_of_step(t) * ntiles;
       const bool second = i >= n0;
       qt = second ? seg.begin1 + (i - n0) : seg.begin0 + i;
-      // The pair's intervals for the tile's half.  At D >= 192 they are
-      // derived here: selected from the two halves' copies, they ended up
-      // read through a table of addresses in scratch memory.  (The copies
+      // The pair's intervals for the tile's half.  With 32-row tiles they
+      // are derived here: selected from the two halves' copies, they ended
+      // up read through a table of addresses in scratch memory.  (The copies
       // measured slightly faster at the other widths.)
       int cf, hf, cl, hl;
-      if constexpr (C::WIDE) {
+      if constexpr (C::BQ == 32) {
         const int qh = second ? seg.half1 : seg.half0;
         col_interval_of_block(n, qh, kh, kblk_f0, kblk_f1, cf, hf);
         col_interval_of_block(n, qh, kh, kblk_l0, kblk_l1, cl, hl);
