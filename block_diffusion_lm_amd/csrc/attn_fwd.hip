@@ -61,8 +61,9 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
 // D = 192 and 256: 32-key K / V tiles, so that two workgroups fit a CU's
-// LDS (Q and O take most of half a register file).
-__global__ __launch_bounds__(64 * NW, (NW == 4 && (D < 192 || BN == 32) ? 2 : 1)) void fwd_kernel(AttnArgs a, int qtiles) {
+// LDS (Q and O take most of half a register file).  D = 64: at most 128
+// registers, four workgroups per CU.
+__global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (NW == 4 && (D < 192 || BN == 32) ? 2 : 1))) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
