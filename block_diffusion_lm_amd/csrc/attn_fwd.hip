@@ -60,10 +60,11 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // SC: softcapping on (the scores are capped before the mask and the
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
-// D = 192 and 256: 32-key K / V tiles, so that two workgroups fit a CU's
-// LDS (Q and O take most of half a register file).  D = 64: at most 128
+// D = 128: 32-key K / V tiles (32 KiB of LDS) and at most 168 registers,
+// three workgroups per CU.  D = 192 and 256: 32-key tiles, two workgroups
+// per CU (Q and O take most of half a register file).  D = 64: at most 128
 // registers, four workgroups per CU.
-__global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (NW == 4 && (D < 192 || BN == 32) ? 2 : 1))) void fwd_kernel(AttnArgs a, int qtiles) {
+__global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 : (NW == 4 && (D < 192 || BN == 32) ? 2 : 1))) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
@@ -148,9 +149,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (NW == 4 && (D < 192 || BN 
   row_interval(g, qh, seg.half1, max(pw1 - 1, pw0), lo_l1, hi_l1);
   row_interval(g, qh, seg.half1, p, lo_p1, hi_p1);
   // The blocks of the wave's first and last rows and of this lane's row.
-  // At D >= 192 the intervals of a tile's half are derived from these per
-  // tile: selected from the two halves' copies, they ended up read through
-  // a table of addresses in scratch memory.
+  // At D >= 192 and with 32-key tiles the intervals of a tile's half are
+  // derived from these per tile: selected from the two halves' copies, they
+  // ended up read through a table of addresses in scratch memory.
   const int bs_f = g.bstart(pw0), be_f = g.bend(pw0);
   const int bs_l = g.bstart(max(pw1 - 1, pw0)), be_l = g.bend(max(pw1 - 1, pw0));
   const int bs_p = g.bstart(p), be_p = g.bend(p);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (NW == 4 && (D < 192 || BN 
       const bool second = i >= n0;
       const int k0 = (second ? seg.begin1 + (i - n0) : seg.begin0 + i) * BN;
       int lf, hf, ll, hl, lo, hi;
-      if constexpr (D >= 192) {
+      if constexpr (D >= 192 || BN == 32) {
         const int kh = second ? seg.half1 : seg.half0;
         row_interval_of_block(qh, kh, bs_f, be_f, lf, hf);
         row_interval_of_block(qh, kh, bs_l, be_l, ll, hl);
@@ -351,7 +352,7 @@ hipError_t launch_fwd(const AttnArgs& a, int D, hipStream_t s) {
   if (D == 96) return launch_fwd_t<96, 64, 4, 2>(a, s);
   if (D == 192) return launch_fwd_t<192, 32, 4, 2>(a, s);
   if (D == 256) return launch_fwd_t<256, 32, 4, 2>(a, s);
-  return launch_fwd_t<128, BDATTN_FWD_BN, BDATTN_FWD_NW, BDATTN_FWD_NBUF>(a, s);
+  return launch_fwd_t<128, 32, 4, 2>(a, s);
 }
 
 }  // namespace bd
