@@ -865,22 +865,26 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Fewer dK/dV workgroups than this leave CUs idle or the tail unbalanced
-// (4 per CU on 256 CUs).
-constexpr long long kDkdvMinBlocks = 1024;
+// Fewer dK/dV workgroups than four per resident slot (256 CUs times the
+// workgroups one CU holds) leave CUs idle or the tail unbalanced.
+constexpr long long kDkdvMinBlocksPerSlot = 4 * 256;
 
 int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
   static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV && DkdvCfg<96>::BKV == DkdvCfg<128>::BKV &&
                     DkdvCfg<192>::BKV == DkdvCfg<128>::BKV,
                 "one key tile size below D = 256");
+  static_assert(DkdvCfg<96>::WGS == DkdvCfg<128>::WGS && DkdvCfg<192>::WGS == DkdvCfg<128>::WGS &&
+                    DkdvCfg<256>::WGS == DkdvCfg<128>::WGS,
+                "one occupancy apart from D = 64");
   const int bkv = D == 256 ? DkdvCfg<256>::BKV : DkdvCfg<128>::BKV;
+  const long long min_blocks = kDkdvMinBlocksPerSlot * (D == 64 ? DkdvCfg<64>::WGS : DkdvCfg<128>::WGS);
   const long long ktiles = ((long long)n + bkv - 1) / bkv;
   const long long base = ktiles * nhalves * B * Hkv;
   int S = 1;
   for (int c = 1; c <= G; ++c) {
     if (G % c) continue;
     S = c;
-    if (base * c >= kDkdvMinBlocks) break;
+    if (base * c >= min_blocks) break;
   }
   return S;
 }

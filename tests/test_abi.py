@@ -144,21 +144,24 @@ def test_grouped_binding_checks_kv_shapes():
 def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     """Statistics (two float32 per query row) plus, when the dK/dV kernel
     splits the groups, float32 partial dK and dV per split.  The split count
-    is the smallest divisor S of G = H / Hkv giving at least 1024 dK/dV
-    workgroups of 128 keys, 64 at D = 256 (all of G when none does)."""
+    is the smallest divisor S of G = H / Hkv giving at least four dK/dV
+    workgroups (of 128 keys, 64 at D = 256) per resident slot: 1024, or 2048
+    at D = 64 where a CU holds two (all of G when none does)."""
     T = n if causal else 2 * n
     r256 = lambda x: -(-x // 256) * 256
     bkv = 64 if D == 256 else 128
     base = -(-n // bkv) * (1 if causal else 2) * B * Hkv
     G = H // Hkv
-    S = next((c for c in range(1, G + 1) if G % c == 0 and base * c >= 1024), G)
+    need = 2048 if D == 64 else 1024
+    S = next((c for c in range(1, G + 1) if G % c == 0 and base * c >= need), G)
     part = 2 * S * B * T * Hkv * D * 4 if S > 1 else 0
     return r256(2 * B * H * T * 4) + r256(part), S
 
 
 @pytest.mark.parametrize("B,n,H,Hkv,D", [
     (8, 1024, 32, 8, 128),   # 1024 workgroups unsplit: S = 1
-    (4, 2048, 16, 1, 64),    # multi-query, 128 workgroups: S = 8
+    (4, 2048, 16, 1, 64),    # multi-query, 128 workgroups: S = 16
+    (8, 2048, 16, 1, 64),    # 256 workgroups: S = 8
     (2, 100, 4, 2, 64),      # tiny: every query head on its own, S = G
     (1, 7, 8, 2, 128),
     (3, 5000, 12, 12, 64),   # plain multi-head
