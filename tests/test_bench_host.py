@@ -105,3 +105,11 @@ def test_cpu_baseline_record():
     assert f"{n * n + n * b} visible pairs" in rec["sample"]
     assert "4 chunks" in rec["sample"]  # 32 rows in chunks of 10
     assert math.isfinite(rec["value"])
+
+
+def test_roofline_at_the_sampled_clock():
+    """The peak scales with the engine clock: at 1.2 GHz half of it."""
+    r = bench.at_clock({"achieved": 1000.0, "peak": 2500.0}, {"median_mhz": 1200.0})
+    assert r["peak_at_median_sclk"] == pytest.approx(1250.0)
+    assert r["frac_at_median_sclk"] == pytest.approx(0.8)
+    assert set(bench.at_clock({"achieved": 1.0, "peak": 2.0}, None)) == {"achieved", "peak"}
