@@ -154,9 +154,12 @@ int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out
  * the workspace, and a reduction adds the partials in a fixed order: the
  * result is still deterministic.  The *_gqa_workspace_size functions
  * return the bytes this needs: the per-row statistics of the plain entry
- * points, plus the partials when the groups are split (at most about
- * 2 * 1024 * 128 * D * 4 bytes, since groups are split only for small
- * problems).  They return 0 on bad sizes.
+ * points, plus the partials when the groups are split: about
+ * 2 * W * K * D * 4 bytes for a split grid of W dK/dV workgroups of K
+ * keys each (K = 128, or 64 at D = 256), where
+ * groups are split only while the unsplit grid is under 1024 workgroups
+ * (2048 at D = 64), so W stays below 4096 when H / H_kv is a power of two.
+ * They return 0 on bad sizes.
  */
 size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D);
 size_t causal_attn_bwd_gqa_workspace_size(int B, int S, int H, int H_kv, int D);
