@@ -98,15 +98,18 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
 // ring fits LDS; D = 256 also runs two pairs only (one wave per SIMD, each
 // with the whole register file), while D = 192 still fits two waves per SIMD.
 // D = 64 streams 32-row tiles too: its LDS (42 KiB) and registers (at most
-// 128) then fit two workgroups per CU, four waves per SIMD.
-template <int D>
+// 128) then fit two workgroups per CU, four waves per SIMD.  So does D = 96
+// (54 KiB), except with softcapping, whose extra per-score work does not fit
+// 128 registers: that instance keeps 64-row tiles at one workgroup per CU.
+template <int D, bool SC = false>
 struct DkdvCfg {
   static constexpr bool WIDE = D >= 192;
-  static constexpr int WGS = D == 64 ? 2 : 1;  // workgroups per CU
+  static constexpr bool SHORT = D == 64 || (D == 96 && !SC);  // 32-row tiles, two workgroups per CU
+  static constexpr int WGS = SHORT ? 2 : 1;  // workgroups per CU
   static constexpr int NPAIR = D == 256 ? 2 : 4;
   static constexpr int NT = 128 * NPAIR;  // 8 waves (4 at D = 256)
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
-  static constexpr int BQ = (WIDE || D == 64) ? 32 : 64;  // query rows per streamed tile
+  static constexpr int BQ = (WIDE || SHORT) ? 32 : 64;  // query rows per streamed tile
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -128,8 +131,9 @@ struct DkdvCfg {
 // P-wave recomputes P from the capped scores and publishes
 // P (1 - tanh^2), so that the dS-wave's dS carries the cap's derivative).
 template <int D, bool GROUPED, bool SC>
-__global__ __launch_bounds__(DkdvCfg<D>::NT, DkdvCfg<D>::WGS) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
-  using C = DkdvCfg<D>;
+__global__ __launch_bounds__((DkdvCfg<D, SC>::NT), (DkdvCfg<D, SC>::WGS)) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
+  using C = DkdvCfg<D, SC>;
+  static_assert(C::NT == DkdvCfg<D>::NT && C::BKV == DkdvCfg<D>::BKV, "one grid for both instances");
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NBUF * C::BUF];
   __shared__ __attribute__((aligned(16))) float fsm[C::NBUF * C::FBUF];
@@ -866,18 +870,21 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
 }
 
 // Fewer dK/dV workgroups than four per resident slot (256 CUs times the
-// workgroups one CU holds) leave CUs idle or the tail unbalanced.
+// workgroups one CU holds) leave CUs idle or the tail unbalanced.  The
+// count follows the uncapped instances (the softcapped D = 96 one holds one
+// workgroup per CU, not two), so that the workspace size does not depend on
+// the cap.
 constexpr long long kDkdvMinBlocksPerSlot = 4 * 256;
 
 int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
   static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV && DkdvCfg<96>::BKV == DkdvCfg<128>::BKV &&
                     DkdvCfg<192>::BKV == DkdvCfg<128>::BKV,
                 "one key tile size below D = 256");
-  static_assert(DkdvCfg<96>::WGS == DkdvCfg<128>::WGS && DkdvCfg<192>::WGS == DkdvCfg<128>::WGS &&
+  static_assert(DkdvCfg<96>::WGS == DkdvCfg<64>::WGS && DkdvCfg<192>::WGS == DkdvCfg<128>::WGS &&
                     DkdvCfg<256>::WGS == DkdvCfg<128>::WGS,
-                "one occupancy apart from D = 64");
+                "one occupancy for D <= 96, one above");
   const int bkv = D == 256 ? DkdvCfg<256>::BKV : DkdvCfg<128>::BKV;
-  const long long min_blocks = kDkdvMinBlocksPerSlot * (D == 64 ? DkdvCfg<64>::WGS : DkdvCfg<128>::WGS);
+  const long long min_blocks = kDkdvMinBlocksPerSlot * (D <= 96 ? DkdvCfg<64>::WGS : DkdvCfg<128>::WGS);
   const long long ktiles = ((long long)n + bkv - 1) / bkv;
   const long long base = ktiles * nhalves * B * Hkv;
   int S = 1;

@@ -47,6 +47,7 @@ struct FwdCfg {
   static constexpr int DB = D / 32;   // 32-wide column blocks of the head dimension
   static constexpr int KB = BN / 32;  // 32-key blocks per key tile
   using Tile = DirectTile<BN, D, NT>;
+  static_assert(Tile::SLOTS % NT == 0, "the counted tile waits assume PER loads per tile in every wave");
   static constexpr int BUF = 2 * Tile::ELEMS;  // K then V
 };
 

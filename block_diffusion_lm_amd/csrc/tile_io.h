@@ -126,9 +126,10 @@ template <int ROWS, int D, int NT>
 struct DirectTile {
   static constexpr int CH = D / 8;
   static constexpr int SLOTS = ROWS * CH;
-  static constexpr int PER = SLOTS / NT;
+  static constexpr int PER = (SLOTS + NT - 1) / NT;
   static constexpr int ELEMS = ROWS * D;
-  static_assert(SLOTS % NT == 0, "tile must split evenly over the threads");
+  // whole waves: the last pass, when partial, is skipped by entire waves
+  static_assert(SLOTS % 64 == 0 && NT % 64 == 0, "tile must split into whole waves");
 
   // lds: LDS byte address of the tile (lds_byte_addr)
   __device__ __forceinline__ static void load(rsrc_t src, uint32_t row_bytes, int row0, uint32_t lds,
@@ -136,6 +137,7 @@ struct DirectTile {
     const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      if (SLOTS % NT != 0 && i == PER - 1 && i * NT + wbase >= SLOTS) break;
       const int slot = i * NT + tid;
       const int r = slot / CH;
       const int c = (slot % CH) ^ swz<D>(r);

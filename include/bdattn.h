@@ -158,7 +158,8 @@ int causal_attn_bwd(const void* q, const void* k, const void* v, const void* out
  * 2 * W * K * D * 4 bytes for a split grid of W dK/dV workgroups of K
  * keys each (K = 128, or 64 at D = 256), where
  * groups are split only while the unsplit grid is under 1024 workgroups
- * (2048 at D = 64), so W stays below 4096 when H / H_kv is a power of two.
+ * (2048 at D = 64 and 96), so W stays below 4096 when H / H_kv is a power
+ * of two.
  * They return 0 on bad sizes.
  */
 size_t diffusion_attn_bwd_gqa_workspace_size(int B, int n, int H, int H_kv, int D);

@@ -146,13 +146,13 @@ def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     splits the groups, float32 partial dK and dV per split.  The split count
     is the smallest divisor S of G = H / Hkv giving at least four dK/dV
     workgroups (of 128 keys, 64 at D = 256) per resident slot: 1024, or 2048
-    at D = 64 where a CU holds two (all of G when none does)."""
+    at D = 64 and 96 where a CU holds two (all of G when none does)."""
     T = n if causal else 2 * n
     r256 = lambda x: -(-x // 256) * 256
     bkv = 64 if D == 256 else 128
     base = -(-n // bkv) * (1 if causal else 2) * B * Hkv
     G = H // Hkv
-    need = 2048 if D == 64 else 1024
+    need = 2048 if D <= 96 else 1024
     S = next((c for c in range(1, G + 1) if G % c == 0 and base * c >= need), G)
     part = 2 * S * B * T * Hkv * D * 4 if S > 1 else 0
     return r256(2 * B * H * T * 4) + r256(part), S
@@ -169,6 +169,7 @@ def _expected_gqa_workspace(B, n, H, Hkv, D, causal=False):
     (1, 1000, 8, 1, 256),
     (2, 4096, 16, 2, 192),   # 512 workgroups of 128 keys: S = 2
     (2, 900, 12, 3, 96),
+    (4, 2048, 16, 2, 96),    # 256 workgroups: S = 8 (1024 would give 4)
 ])
 def test_gqa_workspace_sizes(B, n, H, Hkv, D):
     want, S = _expected_gqa_workspace(B, n, H, Hkv, D)
