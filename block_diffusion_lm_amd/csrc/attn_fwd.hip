@@ -172,7 +172,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) o[i] = zero16();
   float m_run = -INFINITY;  // running maximum, base-2 units, scale applied
-  float l_run = 0.f;        // this lane's share of the denominator
+  float l_run = 0.f;        // this lane's share of the denominator (float32 P: the LSE)
+  float lr_run = 0.f;       // the same sum over P as rounded to bf16 for P.V (normalises O)
 
   // Per-lane parts of the LDS addresses, fixed for the whole walk: one
   // entry per chunk position within the swizzle's span (k-step s reads
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 
         // (including rows that have seen no key yet, where both are -inf)
         const float alpha = (m_cand > m_run) ? fast_exp2(m_run - m_cand) : 1.f;
         l_run *= alpha;
+        lr_run *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 
           l_run += pr;
         }
         const bf16x8 pb0 = pack_bf16x8(sc[kb], 0), pb1 = pack_bf16x8(sc[kb], 8);
+        lr_run = sum_bf16x8(pb0, sum_bf16x8(pb1, lr_run));
         mfma_burst_begin();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -307,10 +310,16 @@ __global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 
     });
   }
 
-  // Epilogue: O = z / l, LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = z / l~, LSE = (m + log2 l) * ln 2.  z sums the bf16
+  // probabilities times V, so dividing by their own sum l~ makes O a
+  // weighted average of the V rows with weights that sum to one: the
+  // rounding of P then moves O by at most 2^-9 sum_j w_j |v_j - O| instead
+  // of 2^-9 sum_j w_j |v_j| (which, in a row dominated by one key whose
+  // probability was rounded above a stale maximum, approaches 2^-9 |O|).
+  // The LSE keeps the float32 sum.
   const float l_tot = halves_sum(l_run);
   if (wave_active && p < n) {
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / halves_sum(lr_run);
     uint16_t* orow = a.out + (sample0 + qoff + p) * rs + (size_t)hh * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)

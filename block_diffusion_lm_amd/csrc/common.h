@@ -55,6 +55,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
   return r;
 }
 
+// acc + the sum of eight bf16 values (exact products with 1.0, float32
+// accumulation): four v_dot2c_f32_bf16 against the pair (1, 1).
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& x, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+  return acc;
+}
+
 // Reductions between lane l and lane l ^ 32.  v_permlane32_swap with the
 // same register as both operands leaves, in every lane, its own value in one
 // result and the other half's value in the other; combining both results
