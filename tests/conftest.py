@@ -8,3 +8,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # BDATTN_PARITY_REPORT=<file>: write the errors the GPU parity checks
+    # measured (tests/parity_report.py) to that JSON file
+    path = os.environ.get("BDATTN_PARITY_REPORT")
+    if path:
+        import parity_report
+        if parity_report.RECORDS:
+            parity_report.write(path)
