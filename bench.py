@@ -86,52 +86,100 @@ def parse():
     return ap.parse_args()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_chunk(task):
+    """One unit of the CPU baseline, run in a worker process with one BLAS
+    thread: the oracle's forward and backward of query rows [r0, r1) of one
+    (sample, head) against all 2n keys.  q, k, v, dout arrive as the bf16
+    bit patterns (uint16)."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_limits
+    qb, kb, vb, db, n, b, r0, r1 = task
+    with threadpool_limits(1):
+        qh, kh, vh, dh = (oracle.to_f64(torch.from_numpy(x).view(torch.bfloat16)) for x in (qb, kb, vb, db))
+        scale = 1.0 / math.sqrt(qh.shape[1])
+        rows = np.arange(r0, r1)
+        M = oracle.block_diffusion_mask(n, b, rows)
+        t0 = time.perf_counter()
+        oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
+        t1 = time.perf_counter()
+        oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
+        t2 = time.perf_counter()
+    return int(M.sum()), t1 - t0, t2 - t1
+
+
 def cpu_baseline(heads, name, target_s=10.0, chunk=2048):
     """Time the float64 oracle (as it stands) on a bounded sample of the same
-    workload: whole (sample, head) problems, taken in the order ``heads``
-    yields them (q, k, v, dout of one head as bf16 CPU tensors, the half
-    length n and the block size b), each processed in chunks of query rows
-    (forward and backward of each chunk against all 2n keys), until about
-    target_s seconds of CPU work have been done."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = 1
-    pairs, chunks, done_heads, D = 0, 0, 0, None
+    workload, on every host core: a pool of len(os.sched_getaffinity(0))
+    worker processes, one BLAS thread each, takes chunks of query rows of
+    whole (sample, head) problems (forward and backward of each chunk
+    against all keys of its sample) in the order ``heads`` yields them (q,
+    k, v, dout of one head as bf16 CPU tensors, the half length n and the
+    block size b), until about target_s seconds of wall time have passed.
+    The rate is the chunks' visible-pair flops (3.5 x 4 x pairs x D) over
+    the wall time of the pool.  Runs before anything touches the GPU: the
+    workers are started fresh ("spawn"), never from a process holding GPU
+    state."""
+    import concurrent.futures
+    import multiprocessing
+
+    cores = len(os.sched_getaffinity(0))
+
+    def tasks():
+        for qh, kh, vh, dh, n, b in heads:
+            bits = tuple(x.contiguous().view(__import__("torch").int16).numpy().view("uint16")
+                         for x in (qh, kh, vh, dh))
+            for r0 in range(0, 2 * n, chunk):
+                yield bits + (n, b, r0, min(r0 + chunk, 2 * n)), qh.shape[1]
+
+    it = tasks()
+    pairs = flops = chunks = 0
     t_fwd = t_bwd = 0.0
-    t_start = time.perf_counter()
-    for qh, kh, vh, dh, n, b in heads:
-        qh, kh, vh, dh = (oracle.to_f64(x) for x in (qh, kh, vh, dh))
-        D = qh.shape[1]
-        scale = 1.0 / math.sqrt(D)
-        for r0 in range(0, 2 * n, chunk):
-            rows = np.arange(r0, min(r0 + chunk, 2 * n))
-            M = oracle.block_diffusion_mask(n, b, rows)
-            pairs += int(M.sum())
-            t0 = time.perf_counter()
-            oracle.masked_attention_forward(qh[rows], kh, vh, M, scale)
-            t1 = time.perf_counter()
-            oracle.masked_attention_backward(qh[rows], kh, vh, dh[rows], M, scale)
-            t2 = time.perf_counter()
-            t_fwd += t1 - t0
-            t_bwd += t2 - t1
-            chunks += 1
-        done_heads += 1
-        if time.perf_counter() - t_start >= target_s:
-            break
-    flops = 3.5 * 4 * pairs * D
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(cores, mp_context=ctx) as ex:
+        ex.submit(int, 0).result()  # workers up before the clock starts
+        t_start = time.perf_counter()
+        running = {}
+        for _ in range(cores):
+            nxt = next(it, None)
+            if nxt is not None:
+                running[ex.submit(_oracle_chunk, nxt[0])] = nxt[1]
+        while running:
+            done, _ = concurrent.futures.wait(running, return_when=concurrent.futures.FIRST_COMPLETED)
+            for fut in done:
+                D = running.pop(fut)
+                p, tf, tb = fut.result()
+                pairs += p
+                flops += 3.5 * 4 * p * D
+                t_fwd += tf
+                t_bwd += tb
+                chunks += 1
+                if time.perf_counter() - t_start < target_s:
+                    nxt = next(it, None)
+                    if nxt is not None:
+                        running[ex.submit(_oracle_chunk, nxt[0])] = nxt[1]
+        wall = time.perf_counter() - t_start
     return {
-        "value": flops / (t_fwd + t_bwd) / 1e12,
+        "value": flops / wall / 1e12,
         "unit": "TFLOPS",
-        "cores": int(cores),
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"float64 oracle forward + backward of {done_heads} whole (sample, head) pair(s) of {name} "
-                   f"({chunks} chunks of up to {chunk} query rows against all keys of their sample; "
-                   f"{pairs} visible pairs); {t_fwd:.1f} s forward + {t_bwd:.1f} s backward; "
-                   f"BLAS threads {cores}; host {platform.processor() or platform.machine()}"),
+        "sample": (f"float64 oracle forward + backward of {chunks} chunks of up to {chunk} query rows of {name} "
+                   f"(each against all keys of its sample; {pairs} visible pairs), whole (sample, head) "
+                   f"problems in order; {cores} worker processes, one BLAS thread each, {wall:.1f} s wall "
+                   f"({t_fwd:.1f} s forward + {t_bwd:.1f} s backward of worker time); CPU {_cpu_model()}"),
     }
 
 
@@ -209,13 +257,37 @@ def mark(ev, i):
         ev[i].record()
 
 
-def setup_batched(w, dev, torch, bd, softcap=0.0):
+def cpu_inputs(w):
+    """The workload's seeded CPU tensors (q, k, v, dout[, cu_seqlens])."""
+    from workloads import VARLEN_WORKLOADS, make_varlen_workload_inputs, make_workload_inputs
+    if w.name in VARLEN_WORKLOADS:
+        return make_varlen_workload_inputs(w)
+    return make_workload_inputs(w)
+
+
+def cpu_heads(w, cpu):
+    """(q, k, v, dout, n, b) of each (sample, head) of the CPU inputs; packed
+    samples longest first."""
+    from workloads import VARLEN_WORKLOADS
+    G = w.H // w.kv_heads
+    if w.name in VARLEN_WORKLOADS:
+        ns, cu = w.half_lengths, cpu[4]
+        for bi in sorted(range(w.B), key=lambda i: -ns[i]):
+            s0, s1 = cu[bi], cu[bi + 1]
+            for hi in range(w.H):
+                yield (cpu[0][s0:s1, hi], cpu[1][s0:s1, hi // G], cpu[2][s0:s1, hi // G], cpu[3][s0:s1, hi],
+                       ns[bi], w.b)
+        return
+    for bi in range(w.B):
+        for hi in range(w.H):
+            yield cpu[0][bi, :, hi], cpu[1][bi, :, hi // G], cpu[2][bi, :, hi // G], cpu[3][bi, :, hi], w.n, w.b
+
+
+def setup_batched(w, dev, torch, bd, cpu, softcap=0.0):
     """(B, 2n, H, D) tensors; the yardstick views them as (2B, n, H, D).
     softcap > 0 runs both through the general entry points with that cap."""
-    from workloads import make_workload_inputs
     B, n, H, Hkv, D, b = w.B, w.n, w.H, w.kv_heads, w.D, w.b
     scale = 1.0 / math.sqrt(D)
-    cpu = make_workload_inputs(w)
     q, k, v, do = (x.to(dev) for x in cpu)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, 2 * n), dtype=torch.float32, device=dev)
@@ -287,30 +359,23 @@ def setup_batched(w, dev, torch, bd, softcap=0.0):
                 "note": "ungrouped = the same kernels on key/value heads repeated to H, "
                         "without the dK/dV reduction over the group"}
 
-    def cpu_heads():
-        G = H // Hkv
-        for bi in range(B):
-            for hi in range(H):
-                yield cpu[0][bi, :, hi], cpu[1][bi, :, hi // G], cpu[2][bi, :, hi // G], cpu[3][bi, :, hi], n, b
-
     P = visible_pairs(n, b)
     assert P == bd.bdattn_visible_pairs(MD, n, b)
     return Problem(diffusion_step=diffusion_step, causal_step=causal_step, ungrouped=ungrouped,
-                   cpu_heads=cpu_heads, pair_heads=P * H * B, causal_pair_heads=n * (n + 1) // 2 * H * 2 * B,
+                   pair_heads=P * H * B, causal_pair_heads=n * (n + 1) // 2 * H * 2 * B,
                    config={"workload": w.describe(), "global_batch": B, "seq_len": 2 * n, "block_size": b,
                            "heads": H, "kv_heads": Hkv, "headdim": D, "softcap": softcap,
                            "parallelism": "single-gpu"})
 
 
-def setup_varlen(w, dev, torch, bd):
+def setup_varlen(w, dev, torch, bd, cpu):
     """Packed samples of random lengths; the yardstick packs the same bytes
     as 2B causal sequences (each half of each sample)."""
-    from workloads import cu_seqlens, make_varlen_workload_inputs
+    from workloads import cu_seqlens
     ns = w.half_lengths
     B, H, Hkv, D, b = w.B, w.H, w.kv_heads, w.D, w.b
     max_n = max(ns)
     scale = 1.0 / math.sqrt(D)
-    cpu = make_varlen_workload_inputs(w)
     q, k, v, do = (x.to(dev) for x in cpu[:4])
     cu = cpu[4]
     total = cu[-1]
@@ -349,17 +414,9 @@ def setup_varlen(w, dev, torch, bd):
                                 H, Hkv, D, 1, scale, 0.0, cws, cws_bytes)
             mark(ev, 2 + stage)
 
-    def cpu_heads():
-        G = H // Hkv
-        for bi in sorted(range(B), key=lambda i: -ns[i]):
-            s0, s1 = cu[bi], cu[bi + 1]
-            for hi in range(H):
-                yield (cpu[0][s0:s1, hi], cpu[1][s0:s1, hi // G], cpu[2][s0:s1, hi // G], cpu[3][s0:s1, hi],
-                       ns[bi], b)
-
     P = sum(visible_pairs(nb, b) for nb in ns if nb > 0)
     return Problem(diffusion_step=diffusion_step, causal_step=causal_step, ungrouped=lambda: None,
-                   cpu_heads=cpu_heads, pair_heads=P * H,
+                   pair_heads=P * H,
                    causal_pair_heads=sum(nb * (nb + 1) for nb in ns) * H,
                    config={"workload": w.describe(), "global_batch": B, "seq_len": 2 * max_n,
                            "total_tokens": total, "block_size": b, "heads": H, "kv_heads": Hkv,
@@ -475,6 +532,14 @@ def main():
         known = ", ".join(list(batched) + list(VARLEN_WORKLOADS))
         print(f"unknown workload {args.workload!r}; known: {known}", file=sys.stderr)
         sys.exit(2)
+    # The CPU baseline runs first: its worker processes start before anything
+    # in this process touches the GPU.
+    cpu = None
+    inputs = None
+    if not args.fp8:
+        inputs = cpu_inputs(w)
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(cpu_heads(w, inputs), w.name, args.cpu_seconds)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.fp8:
@@ -486,7 +551,7 @@ def main():
     if args.softcap and setup is not setup_batched:
         print("--softcap takes a batched workload", file=sys.stderr)
         sys.exit(2)
-    prob = setup_batched(w, dev, torch, bd, args.softcap) if args.softcap else setup(w, dev, torch, bd)
+    prob = setup_batched(w, dev, torch, bd, inputs, args.softcap) if args.softcap else setup(w, dev, torch, bd, inputs)
     D = w.D
 
     # ---- warm-up, then exactly K timed steps --------------------------------
@@ -583,10 +648,6 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(prob.cpu_heads(), w.name, args.cpu_seconds)
 
     line = {
         "metric": "fwd+bwd TFLOPS (visible pairs only) and ratio vs own causal kernel on 2B×n",
