@@ -28,6 +28,7 @@ SIGNATURES = {
     "diffusion_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "diffusion_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "diffusion_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "diffusion_attn_bwd_noalloc": (_i, [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _vp]),
     "causal_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]),
     "causal_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i]),
     "causal_attn_bwd": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _vp, _sz, _vp]),
@@ -142,6 +143,22 @@ def diffusion_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_si
                                     float(scale), _ptr(workspace), int(workspace_bytes),
                                     _stream_handle(q, stream)),
            "diffusion_attn_bwd")
+
+
+def diffusion_attn_bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, B, n, H, D, block_size, scale,
+                               stream=None):
+    """diffusion_attn_bwd without a workspace: the library keeps the row
+    statistics in its own static device array (calls that overlap on one GPU
+    race; see the header)."""
+    bf = torch.bfloat16
+    qs = (B, 2 * n, H, D)
+    _want(("q", q, bf, qs), ("k", k, bf, qs), ("v", v, bf, qs), ("out", out, bf, qs),
+          ("dout", dout, bf, qs), ("lse", lse, torch.float32, (B, H, 2 * n)), ("dq", dq, bf, qs),
+          ("dk", dk, bf, qs), ("dv", dv, bf, qs))
+    _check(lib().diffusion_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), B, n, H, D, block_size,
+                                            float(scale), _stream_handle(q, stream)),
+           "diffusion_attn_bwd_noalloc")
 
 
 def causal_attn_fwd(q, k, v, out, lse, B, S, H, D, scale, stream=None):

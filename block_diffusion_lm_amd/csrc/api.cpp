@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "bdattn.h"
 #include "geometry.h"
@@ -169,6 +170,44 @@ int run_bwd(const Problem& p, int stage, const void* q, const void* k, const voi
   return e == hipSuccess ? BDATTN_OK : BDATTN_ERR_LAUNCH;
 }
 
+// ---- the static scratch of diffusion_attn_bwd_noalloc ----------------------
+//
+// For callers that cannot allocate: the backward's per-row statistics
+// (-delta and lse2, 8 bytes per query row and head) live in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy (loaded with the code object) until the process ends.
+// Host code never uses the array's name as an address: its device address
+// is looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The device the call's work runs on (the stream's, or the current one for
+// the null stream) and that device's address of scratch.
+int scratch_of(void* stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return BDATTN_ERR_LAUNCH;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess)
+    return BDATTN_ERR_INVALID;
+  if (dev < 0 || dev >= kMaxDevices) return BDATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return BDATTN_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return BDATTN_ERR_LAUNCH;
+    if (e != hipSuccess || p == nullptr) return BDATTN_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return BDATTN_OK;
+}
+
 Problem batched(int mode, int B, int n, int H, int H_kv, int D, int b, float scale) {
   return Problem{mode, B, n, H, H_kv, D, mode == bd::MODE_CAUSAL ? 1 : b, scale, nullptr, 0, 0.f};
 }
@@ -201,6 +240,8 @@ const char* bdattn_status_string(int status) {
     case BDATTN_ERR_INVALID: return "invalid argument";
     case BDATTN_ERR_UNSUPPORTED: return "unsupported head dimension (need 64, 96, 128, 192 or 256) or size";
     case BDATTN_ERR_LAUNCH: return "HIP launch error";
+    case BDATTN_ERR_TOO_LARGE:
+      return "problem needs more than the 32 MiB static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -223,6 +264,23 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        size_t workspace_bytes_, void* stream) {
   return run_bwd(batched(bd::MODE_DIFFUSION, B, n, H, H, D, block_size, scale), -1, q, k, v, out,
                  dout, lse, dq, dk, dv, workspace, workspace_bytes_, stream);
+}
+
+int diffusion_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int B, int n, int H, int D, int block_size, float scale,
+                               void* stream) {
+  const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr || !aligned(ptr, 16)) return BDATTN_ERR_INVALID;
+  const Problem p = batched(bd::MODE_DIFFUSION, B, n, H, H, D, block_size, scale);
+  const int st = check_problem(p);
+  if (st != BDATTN_OK) return st;
+  if (workspace_bytes(p) > kScratchBytes) return BDATTN_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int sst = scratch_of(stream, &ws);
+  if (sst != BDATTN_OK) return sst;
+  return run_bwd(p, -1, q, k, v, out, dout, lse, dq, dk, dv, ws, kScratchBytes, stream);
 }
 
 int causal_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,

@@ -56,6 +56,7 @@ enum {
   BDATTN_ERR_INVALID = 1,      /* null pointer, misaligned pointer, bad size or scale */
   BDATTN_ERR_UNSUPPORTED = 2,  /* head dimension other than 64, 96, 128, 192 or 256 */
   BDATTN_ERR_LAUNCH = 3,       /* the HIP runtime refused a launch */
+  BDATTN_ERR_TOO_LARGE = 4,    /* beyond the static scratch of diffusion_attn_bwd_noalloc */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -97,6 +98,31 @@ int diffusion_attn_bwd(const void* q, const void* k, const void* v, const void* 
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
                        int B, int n, int H, int D, int block_size, float scale,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffusion_attn_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the per-row statistics
+ * (8 bytes per query row and head) kept in a static device array of the
+ * library instead of a caller workspace.  Arguments as diffusion_attn_bwd,
+ * without the workspace.
+ *   Limit: B * H * 2n <= 4194304 query rows x heads (the array is 32 MiB);
+ *   larger problems return BDATTN_ERR_TOO_LARGE and launch nothing.
+ *   The array is per GPU: each GPU the library runs on holds its own copy
+ *   until the process ends.  The first call on a device looks up its
+ *   address there (no allocation); the call runs on the stream's device
+ *   (the current device for a NULL stream).
+ *   Every call on one GPU uses that GPU's one array, so calls that overlap
+ *   in time on the same GPU (other streams, other threads) race and corrupt
+ *   each other's results; order them on one stream or with events.  No
+ *   state needs clearing between calls: each call writes the statistics of
+ *   every row before reading them.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ */
+int diffusion_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int B, int n, int H, int D, int block_size, float scale,
+                               void* stream);
 
 /*
  * One stage of the backward pass, for timing the kernels separately.  The
