@@ -153,6 +153,86 @@ def summarize(workload: str, trace: str, fetch: Optional[str], write: Optional[s
         f.write("\n".join(txt) + "\n")
 
 
+# The counter passes behind counters_<workload>.txt (each within one
+# pass's hardware limits: at most 8 SQ, 4 TCC and 2 GRBM counters).
+COUNTER_PASSES = [
+    ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_BANK_CONFLICT"],
+    ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VALU_TRANS_F32",
+     "SQ_WAIT_INST_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"],
+    ["FETCH_SIZE"],
+    ["WRITE_SIZE"],
+]
+NUM_CU = 256      # MI355X compute units
+SIMD_PER_CU = 4
+NUM_XCD = 8       # GRBM_GUI_ACTIVE reads the sum over the 8 XCDs (it is 8x the
+                  # kernel's duration times the clock)
+
+
+def counters_summary(workload: str, trace: str, pmc_dbs, commands, copy_mib: int, out_dir: str) -> str:
+    """Per kernel: the average per dispatch of every counter of
+    COUNTER_PASSES, and what follows from them (see the file's notes)."""
+    stats = {_short(n): s for n, s in kernel_stats(trace).items() if "bd::" in n}
+    vals: Dict[str, Dict[str, float]] = {}
+    copy = {}
+    for db in pmc_dbs:
+        con = sqlite3.connect(db)
+        for name, cname, val in con.execute(
+                "select kernel_name, counter_name, avg(value) from counters_collection "
+                "group by kernel_name, counter_name"):
+            if COPY_SYMBOL in name:
+                copy[cname] = float(val)
+            if "bd::" in name:
+                vals.setdefault(_short(name), {})[cname] = float(val)
+    copy_kib = copy_mib * 1024.0
+    fscale = copy_kib / copy["FETCH_SIZE"] if copy.get("FETCH_SIZE") else None
+    wscale = copy_kib / copy["WRITE_SIZE"] if copy.get("WRITE_SIZE") else None
+    lines = [f"# rocprofv3 counters per dispatch, workload {workload}",
+             f"# kernel sources sha256 (all files): {source_hash()}",
+             "# commands (one counter pass each; the kernel durations from the trace):"]
+    lines += [f"#   {c}" for c in commands]
+    lines += ["# derived:",
+              "#   clock_mhz = GRBM_GUI_ACTIVE / 8 XCDs / duration",
+              "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 256 CU * 4 SIMD):",
+              "#     the share of the matrix cores' cycles spent on MFMAs (32 cycles per 32x32x16 bf16)",
+              "#   mfma_tflops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 flop / duration",
+              "#   valu_per_mfma, lds_per_mfma, salu_per_mfma = instruction counts / SQ_INSTS_MFMA",
+              "#   hbm_gbs = (FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale) KiB / duration,",
+              f"#   scales from a {copy_mib} MiB device copy in the same runs "
+              f"(fetch {fscale if fscale else float('nan'):.3f}, write {wscale if wscale else float('nan'):.3f})",
+              ""]
+    for k in sorted(vals, key=lambda k: -stats.get(k, {"avg_ns": 0})["avg_ns"]):
+        v = vals[k]
+        dur = stats.get(k, {}).get("avg_ns")
+        lines.append(f"[{k}] {dur / 1e3:.1f} us per dispatch" if dur else f"[{k}]")
+        for cname in [c for p in COUNTER_PASSES for c in p]:
+            if cname in v:
+                lines.append(f"  {cname:32s} {v[cname]:.6g}")
+        mf = v.get("SQ_INSTS_MFMA")
+        if v.get("GRBM_GUI_ACTIVE") and dur:
+            lines.append(f"  {'clock_mhz':32s} {v['GRBM_GUI_ACTIVE'] / NUM_XCD / (dur * 1e-9) / 1e6:.0f}")
+        if v.get("SQ_VALU_MFMA_BUSY_CYCLES") and v.get("GRBM_GUI_ACTIVE"):
+            cyc = v["GRBM_GUI_ACTIVE"] / NUM_XCD * NUM_CU * SIMD_PER_CU
+            lines.append(f"  {'mfma_busy':32s} {v['SQ_VALU_MFMA_BUSY_CYCLES'] / cyc:.4f}")
+        if v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") and dur:
+            lines.append(f"  {'mfma_tflops':32s} {v['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / (dur * 1e-9) / 1e12:.1f}")
+        if mf:
+            for cname, label in (("SQ_INSTS_VALU", "valu_per_mfma"), ("SQ_INSTS_LDS", "lds_per_mfma"),
+                                 ("SQ_INSTS_SALU", "salu_per_mfma")):
+                if cname in v:
+                    lines.append(f"  {label:32s} {v[cname] / mf:.3f}")
+        if fscale and wscale and "FETCH_SIZE" in v and "WRITE_SIZE" in v and dur:
+            b = (v["FETCH_SIZE"] * fscale + v["WRITE_SIZE"] * wscale) * 1024.0
+            lines.append(f"  {'hbm_bytes':32s} {b:.4g}")
+            lines.append(f"  {'hbm_gbs':32s} {b / (dur * 1e-9) / 1e9:.1f}")
+        lines.append("")
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, f"counters_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -166,10 +246,23 @@ def main():
     s.add_argument("--write-command", default="")
     s.add_argument("--copy-mib", type=int, default=1024)
     s.add_argument("--out", default="profiles")
+    c = sub.add_parser("counters")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--trace", required=True)
+    c.add_argument("--pmc", nargs="+", required=True, help="one database per counter pass")
+    c.add_argument("--commands", nargs="+", default=[])
+    c.add_argument("--copy-mib", type=int, default=1024)
+    c.add_argument("--out", default="profiles")
+    c2 = sub.add_parser("passes", help="print the counter passes, one per line")
     sub.add_parser("hash")
     a = ap.parse_args()
     if a.cmd == "hash":
         print(source_hash())
+    elif a.cmd == "passes":
+        for p in COUNTER_PASSES:
+            print(" ".join(p))
+    elif a.cmd == "counters":
+        print(counters_summary(a.workload, a.trace, a.pmc, a.commands, a.copy_mib, a.out))
     else:
         summarize(a.workload, a.trace, a.fetch, a.write, a.command, a.out, a.copy_mib,
                   a.fetch_command, a.write_command)

@@ -36,7 +36,9 @@
  *    caller's next synchronisation.
  *  - Arguments are validated before anything is launched; on error nothing
  *    is written and nothing is launched.  The library allocates no memory
- *    and keeps no state between calls, so calls are reentrant.
+ *    and keeps no state between calls, so calls are reentrant; the one
+ *    exception is diffusion_attn_bwd_noalloc, whose calls share a static
+ *    device array per GPU (see there).
  *  - Return value: one of the BDATTN_* status codes below.
  *
  * Outputs are bfloat16 (the inputs' type); accumulation is float32.
