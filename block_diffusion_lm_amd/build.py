@@ -87,4 +87,13 @@ def build(extra_flags=(), verbose: bool = True, out: str = None, source_flags=No
 
 
 if __name__ == "__main__":
-    build(sys.argv[1:])
+    # python -m block_diffusion_lm_amd.build [--out PATH] [hipcc options...]
+    # e.g. --out _build/libbdattn_poison.so -DBDATTN_LDS_POISON for the LDS
+    # poison debug build (load it with BDATTN_LIB=PATH)
+    args = sys.argv[1:]
+    out = None
+    if "--out" in args:
+        i = args.index("--out")
+        out = os.path.abspath(args[i + 1])
+        args = args[:i] + args[i + 2:]
+    build(args, out=out)

@@ -379,6 +379,13 @@ __global__ __launch_bounds__((DkdvCfg<D, SC>::NT), (DkdvCfg<D, SC>::WGS)) void b
           const uint16_t* Tb = smem + slot * C::BUF;
           const float* Ls = fsm + slot * C::FBUF;
           u32x4* px = pex + (j & 1) * C::PXS + pair * (C::QB * 2 * 64) + lane;
+#ifdef BDATTN_LDS_POISON
+          // the dS-wave finished reading this exchange buffer (step j - 2's
+          // P) before the barrier that started this step
+#pragma unroll
+          for (int u = 0; u < C::QB * 2; ++u) px[u * 64] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
           bool act[C::QB], full[C::QB];
           int qt, clo, chi;
           blocks(j, act, full, qt, clo, chi);

@@ -130,7 +130,31 @@ __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
 // LDS buffer is read only after wait_vmem() and a workgroup barrier, and
 // refilled only after the barrier that follows its last reads.  No other
 // code in these kernels keeps a value in M0.
+//
+// Debug build (BDATTN_LDS_POISON): before each such load, every lane first
+// writes NaN over exactly the LDS bytes its load will fill and waits for
+// that write.  A load is only issued once every read of the buffer's old
+// contents is over, so a read that comes too late (after the refill was
+// issued) or too early (before the new tile landed) sees NaN instead of
+// plausible stale data, and the results turn to NaN.
+#ifdef BDATTN_LDS_POISON
+__device__ __forceinline__ void lds_poison(uint32_t lds_wave, uint32_t bytes_per_lane) {
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const uint32_t addr = lds_wave + lane * bytes_per_lane;
+  if (bytes_per_lane == 16) {
+    const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)addr = nan4;
+  } else {
+    *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)addr = 0x7fc00000u;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+#endif
+
 __device__ __forceinline__ void lds_direct16(rsrc_t r, uint32_t lds_wave, uint32_t voff, uint32_t soff) {
+#ifdef BDATTN_LDS_POISON
+  lds_poison(lds_wave, 16);
+#endif
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
@@ -141,6 +165,9 @@ __device__ __forceinline__ void lds_direct16(rsrc_t r, uint32_t lds_wave, uint32
 }
 
 __device__ __forceinline__ void lds_direct4(rsrc_t r, uint32_t lds_wave, uint32_t voff, uint32_t soff) {
+#ifdef BDATTN_LDS_POISON
+  lds_poison(lds_wave, 4);
+#endif
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
