@@ -83,6 +83,190 @@ __device__ __forceinline__ int half_off(const AttnArgs& a, int half, int n) {
   const size_t kvb1 = (sample0 + half_off(a, seg.half1, n)) * rs_kv + (size_t)hk * D;
 
 // ---------------------------------------------------------------------------
+// dK / dV of the noisy keys: the block diagonal of the noisy half.
+// ---------------------------------------------------------------------------
+// Fast Diffusion Attention, "Hopper": the noisy diagonal of the backward
+// pass has a kernel of its own, and the main dK/dV kernel walks the clean
+// key tiles only.  A noisy key is seen by the noisy queries of its own block
+// and by no other query ("Block diffusion in one picture"), so its dK and dV
+// are sums over that block's rows alone.  Each wave owns 32 keys and works
+// alone (no barrier, no exchange with other waves): it holds K and V as B
+// operands, stages the rows of its keys' blocks 32 at a time (Q and dO) in
+// its own LDS region, and per 32-row chunk computes S = Q K^T, P from the
+// saved LSE, dP = dO V^T, dS = P (dP - delta), dV^T += dO^T P and
+// dK^T += Q^T dS (FlashAttention: Exact Attention Without Materialization,
+// section 4.5), one key per lane as in the main kernel.  With grouped heads
+// the wave walks every query head of the group, so dK and dV are written
+// once, in bf16, without partials.
+// The dedicated kernel is a build option (BDATTN_NOISY_DIAG_KERNEL, off by
+// default): on MI355X the main kernel's own noisy key tiles measured faster
+// at every workload tried (its paired waves skip the invisible 32 x 32
+// blocks, and its light noisy workgroups fill the tail of the launch, which
+// a second launch cannot).  With the option, blocks up to kDiagMaxBlock use
+// it; above, a noisy key tile is seen by many rows and the main kernel
+// walks it as usual.
+constexpr int kDiagMaxBlock = 64;
+
+__host__ __device__ inline bool use_noisy_diag(int mode, int b) {
+#ifdef BDATTN_NOISY_DIAG_KERNEL
+  return mode == MODE_DIFFUSION && b <= kDiagMaxBlock;
+#else
+  (void)mode;
+  (void)b;
+  return false;
+#endif
+}
+
+// One wave, keys [k0, k0 + 32) of the noisy half of sample bi, key/value
+// head hk (every query head of its group in turn): pass 0 sums
+// dV^T += dO^T P, pass 1 dK^T += Q^T dS (two waves share the work of one
+// group of keys, so that only one accumulator set is live in each).  Tq
+// and Tg: the wave's LDS regions for 32 rows of Q and of dO.
+template <int D, bool GROUPED, bool SC>
+__device__ __forceinline__ void noisy_diag_wave(const AttnArgs& a, int bi, int hk, int k0, int pass,
+                                                uint16_t* Tq, uint16_t* Tg, int lane) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  using Tile = DirectTile<32, D, 64>;  // one wave's 32-row chunk
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+  size_t sample0, stat0;
+  int n;
+  if (!sample_of(a, bi, sample0, n, stat0) || k0 >= n) return;
+  const Geom g{n, a.b};
+  const int key = k0 + l32;
+  // the rows that see some key of the wave, and those that see this lane's
+  const int r_lo = g.bstart(k0);
+  const int r_hi = g.bend(min(k0 + 31, n - 1));
+  const int clo = key < n ? g.bstart(key) : 0;
+  const int chi = key < n ? g.bend(key) : 0;
+
+  const size_t rs = (size_t)a.H * D;
+  const size_t rs_kv = (size_t)a.Hkv * D;
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  const uint32_t half_bytes = (uint32_t)n * row_bytes;
+  const uint32_t kv_row_bytes = (uint32_t)rs_kv * 2u;
+
+  const size_t kb = sample0 * rs_kv + (size_t)hk * D;
+  const rsrc_t rk = make_rsrc(a.k + kb, (uint32_t)n * kv_row_bytes);
+  const rsrc_t rv = make_rsrc(a.v + kb, (uint32_t)n * kv_row_bytes);
+  const uint32_t lq = __builtin_amdgcn_readfirstlane(lds_byte_addr(Tq));
+  const uint32_t lg = __builtin_amdgcn_readfirstlane(lds_byte_addr(Tg));
+  const Softcap capc = SC ? softcap_consts(a.scale, a.softcap) : Softcap{0.f, 0.f};
+  const int G = GROUPED ? a.G : 1;
+  {
+    bf16x8 xk[KS], xv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t off = (uint32_t)key * kv_row_bytes + (uint32_t)(16 * s + 8 * h2) * 2u;
+      xk[s] = as_bf16x8(buf_ld16(rk, off, 0));
+      if (pass == 1) xv[s] = as_bf16x8(buf_ld16(rv, off, 0));
+    }
+    floatx16 acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = zero16();
+    for (int gi = 0; gi < G; ++gi) {
+      const int hh = hk * G + gi;
+      const size_t qb = sample0 * rs + (size_t)hh * D;
+      const rsrc_t rq = make_rsrc(a.q + qb, half_bytes);
+      const rsrc_t rg = make_rsrc(a.dout + qb, half_bytes);
+      const size_t sb = stat0 + (size_t)hh * a.stat_hs;
+      const rsrc_t rl = make_rsrc(a.lse2 + sb, (uint32_t)n * 4u);
+      const rsrc_t rd = make_rsrc(a.ndelta + sb, (uint32_t)n * 4u);
+      for (int r0 = r_lo; r0 < r_hi; r0 += 32) {
+        // the previous chunk's LDS reads are over (their values fed the
+        // products below); refill the wave's regions
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        Tile::load(rq, row_bytes, r0, lq, lane);
+        Tile::load(rg, row_bytes, r0, lg, lane);
+        wait_vmem();
+        // S = Q K^T (and dP = dO V^T in pass 1); register r holds row
+        // r0 + 8 (r / 4) + 4 h2 + r % 4; rows past the half read lse2 =
+        // -delta = 0 (and Q = dO = 0)
+        floatx16 sc = zero16(), dp;
+        if (pass == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            dp[r] = buf_ldf(rd, (uint32_t)(r0 + 8 * (r >> 2) + 4 * h2 + (r & 3)) * 4u);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sc = mfma32(lds_vec_at(Tq + row8_lane_off<D>(lane, 2 * s)), xk[s], sc);
+          if (pass == 1) dp = mfma32(lds_vec_at(Tg + row8_lane_off<D>(lane, 2 * s)), xv[s], dp);
+        }
+        // P (zero where the row is outside this lane's key's block), or dS
+        floatx16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          const float l2 = buf_ldf(rl, (uint32_t)row * 4u);
+          float p;
+          if constexpr (SC) {
+            const float rr = softcap_r(capc, sc[r]);
+            p = fast_exp2(softcap_y(capc, rr) - l2);
+            if (pass == 1) p *= 4.f * rr * (1.f - rr) * dp[r];
+          } else {
+            p = fast_exp2(__builtin_fmaf(sc[r], a.scale_log2, -l2));
+            if (pass == 1) p *= dp[r];
+          }
+          x[r] = (row >= clo && row < chi) ? p : 0.f;
+        }
+        const bf16x8 xb[2] = {pack_bf16x8(x, 0), pack_bf16x8(x, 8)};
+        // pass 0: dV^T += dO^T P; pass 1: dK^T += Q^T dS
+        const uint16_t* T = pass == 0 ? Tg : Tq;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint16_t* tr = T + 16 * ks * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(lds_trA_at(tr + trA_lane_off<D>(lane, 32 * db, 0), tr + trA_lane_off<D>(lane, 32 * db, 1)),
+                             xb[ks], acc[db]);
+        }
+      }
+    }
+    // lane = key, register r of block db = dimension 32db + 8(r/4) + 4h2 + r%4
+    if (key < n) {
+      const size_t off = (sample0 + key) * rs_kv + (size_t)hk * D;
+      uint16_t* dst = (pass == 0 ? a.dv : a.dk) + off;
+      const float f = pass == 0 ? 1.f : a.scale;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = 32 * db + 8 * gq + 4 * h2;
+          u32x2 pk = {pack2_bf16(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
+                      pack2_bf16(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
+          *reinterpret_cast<u32x2*>(dst + d) = pk;
+        }
+    }
+  }
+}
+
+
+// 4 waves, 64 keys: waves 0 and 1 sum dV for keys 64 kt + 32 w, waves 2
+// and 3 dK for the same keys.  Each wave has 32 rows of Q and of dO in LDS.
+template <int D>
+struct DiagCfg {
+  static constexpr int NT = 256;
+  static constexpr int BKV = 64;
+  static constexpr int CH = 32 * D;  // elements of one 32-row chunk
+};
+
+template <int D, bool GROUPED, bool SC>
+__global__ __launch_bounds__(DiagCfg<D>::NT, 1) void bwd_noisy_diag_kernel(AttnArgs a, int dtiles) {
+  using C = DiagCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * 2 * C::CH];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int BH = a.B * a.Hkv;
+  const int kt = blockIdx.x / BH;
+  const int bi = (blockIdx.x % BH) / a.Hkv;
+  const int hk = (blockIdx.x % BH) % a.Hkv;
+  uint16_t* T = smem + 2 * wv * C::CH;
+  noisy_diag_wave<D, GROUPED, SC>(a, bi, hk, kt * C::BKV + 32 * (wv & 1), wv >> 1, T, T + C::CH,
+                                  threadIdx.x & 63);
+}
+
+// ---------------------------------------------------------------------------
 // dK / dV: key-stationary, one workgroup per 128 keys, 8 waves in 4 pairs.
 // The pair's two waves share 32 keys: the P-wave holds K and computes
 // S = Q K^T, P and dV^T += dO^T P; the dS-wave holds V and computes
@@ -545,18 +729,32 @@ __global__ __launch_bounds__((DkdvCfg<D, SC>::NT), (DkdvCfg<D, SC>::WGS)) void b
 // order, rounded to bf16.  Each thread produces 8 consecutive elements of
 // the [B][T][Hkv][D] outputs; elements [0, E) are dK, [E, 2E) dV.
 // With packed samples (cu non-null) only the tokens [cu[0], cu[B]) belong
-// to samples: the other rows of dK and dV are left as they are.
+// to samples: the other rows of dK and dV are left as they are.  With
+// skip_noisy the rows of noisy halves are left alone too: the noisy-diagonal
+// kernel writes them (T: tokens per sample when batched; packed samples
+// find their sample by bisection of cu).
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                          uint16_t* __restrict__ dk,
                                                          uint16_t* __restrict__ dv, long long E,
-                                                         int S, const int* cu, int B, int row_elems) {
+                                                         int S, const int* cu, int B, int row_elems,
+                                                         int skip_noisy, int T) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= 2 * E) return;
   const bool second = i >= E;
   const long long e = second ? i - E : i;
+  const long long t = e / row_elems;
   if (cu != nullptr) {
-    const long long t = e / row_elems;
     if (t < cu[0] || t >= cu[B]) return;
+    if (skip_noisy) {
+      int lo = 0, hi = B;  // the sample s with cu[s] <= t < cu[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      if (t - cu[lo] < (cu[lo + 1] - cu[lo]) / 2) return;
+    }
+  } else if (skip_noisy && t % T < T / 2) {
+    return;
   }
   const float* src = part + (second ? (long long)S * E : 0) + e;
   float4 lo = *reinterpret_cast<const float4*>(src);
@@ -853,7 +1051,10 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
   } else {
     using KC = DkdvCfg<D>;
     const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
-    const long long kblocks = (long long)ktiles * a.nhalves * a.B * a.Hkv * a.S;
+    // with the noisy-diagonal kernel the main grid holds the clean key tiles
+    // only (they come first in its order)
+    const bool diag = use_noisy_diag(a.mode, a.b);
+    const long long kblocks = (long long)ktiles * (diag ? 1 : a.nhalves) * a.B * a.Hkv * a.S;
     const dim3 grid((unsigned)kblocks), block(KC::NT);
     if (a.softcap > 0.f) {
       if (a.G > 1)
@@ -870,8 +1071,26 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
       const long long E = a.tokens * a.Hkv * D;
       const long long rblocks = (2 * E / 8 + 255) / 256;
       hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, s, a.part, a.dk,
-                         a.dv, E, a.S, a.cu, a.B, a.Hkv * D);
+                         a.dv, E, a.S, a.cu, a.B, a.Hkv * D, diag ? 1 : 0, a.T);
     }
+#ifdef BDATTN_NOISY_DIAG_KERNEL
+    if (diag) {
+      using DC = DiagCfg<D>;
+      const int dtiles = (a.n + DC::BKV - 1) / DC::BKV;
+      const dim3 dgrid((unsigned)((long long)dtiles * a.B * a.Hkv)), dblock(DC::NT);
+      if (a.softcap > 0.f) {
+        if (a.G > 1)
+          hipLaunchKernelGGL((bwd_noisy_diag_kernel<D, true, true>), dgrid, dblock, 0, s, a, dtiles);
+        else
+          hipLaunchKernelGGL((bwd_noisy_diag_kernel<D, false, true>), dgrid, dblock, 0, s, a, dtiles);
+      } else {
+        if (a.G > 1)
+          hipLaunchKernelGGL((bwd_noisy_diag_kernel<D, true, false>), dgrid, dblock, 0, s, a, dtiles);
+        else
+          hipLaunchKernelGGL((bwd_noisy_diag_kernel<D, false, false>), dgrid, dblock, 0, s, a, dtiles);
+      }
+    }
+#endif
   }
   return hipGetLastError();
 }
