@@ -105,6 +105,25 @@ def read_traffic(path: str) -> Optional[dict]:
     return vals
 
 
+def read_counters(path: str) -> Optional[dict]:
+    """Parse a counters_<workload>.txt file: {"source_sha256": ..., kernel:
+    {name: value}} (None when missing)."""
+    if not os.path.exists(path):
+        return None
+    out: dict = {}
+    cur = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# kernel sources sha256 (all files):"):
+                out["source_sha256"] = line.split(":", 1)[1].strip()
+            elif line.startswith("["):
+                cur = out.setdefault(line[1:line.index("]")], {})
+            elif cur is not None and line.startswith("  ") and line.strip():
+                name, val = line.split()
+                cur[name] = float(val)
+    return out
+
+
 def summarize(workload: str, trace: str, fetch: Optional[str], write: Optional[str], command: str,
               out_dir: str, copy_mib: int = 1024, fetch_command: str = "", write_command: str = "") -> None:
     stats = kernel_stats(trace)

@@ -113,3 +113,15 @@ def test_roofline_at_the_sampled_clock():
     assert r["peak_at_median_sclk"] == pytest.approx(1250.0)
     assert r["frac_at_median_sclk"] == pytest.approx(0.8)
     assert set(bench.at_clock({"achieved": 1.0, "peak": 2.0}, None)) == {"achieved", "peak"}
+
+
+def test_committed_counters_parse():
+    """profiles/counters_c4.txt: every kernel has an MFMA-busy share in (0, 1]
+    and a clock; the file names the sources it was taken on."""
+    c = profiling.read_counters(os.path.join(ROOT, "profiles", "counters_c4.txt"))
+    assert c is not None and len(c["source_sha256"]) == 64
+    kernels = {k: v for k, v in c.items() if isinstance(v, dict)}
+    assert set(kernels) == {"fwd", "bwd_dq", "bwd_dkdv"}
+    for v in kernels.values():
+        assert 0 < v["mfma_busy"] <= 1 and 1000 < v["clock_mhz"] < 2600
+        assert v["SQ_LDS_BANK_CONFLICT"] >= 0 and v["hbm_gbs"] > 0
