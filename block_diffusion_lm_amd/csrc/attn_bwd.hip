@@ -267,7 +267,8 @@ __global__ __launch_bounds__(DiagCfg<D>::NT, 1) void bwd_noisy_diag_kernel(AttnA
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-stationary, one workgroup per 128 keys, 8 waves in 4 pairs.
+// dK / dV: key-stationary, one pair of waves per 32 keys; four pairs (128
+// keys, 8 waves) per workgroup unless stated below.
 // The pair's two waves share 32 keys: the P-wave holds K and computes
 // S = Q K^T, P and dV^T += dO^T P; the dS-wave holds V and computes
 // dP = dO V^T, dS = P (dP - delta) and dK^T += Q^T dS.  The dS-wave needs the
@@ -285,15 +286,25 @@ __global__ __launch_bounds__(DiagCfg<D>::NT, 1) void bwd_noisy_diag_kernel(AttnA
 // 128) then fit two workgroups per CU, four waves per SIMD.  So does D = 96
 // (54 KiB), except with softcapping, whose extra per-score work does not fit
 // 128 registers: that instance keeps 64-row tiles at one workgroup per CU.
-template <int D, bool SC = false>
+// Multi-head D = 128 streams 32-row tiles with six pairs (12 waves, 192
+// keys): with 32-row steps a wave needs at most 168 registers, so three waves
+// share a SIMD, and every Q / dO tile serves 192 keys instead of 128 (dK/dV
+// 3% faster than four pairs with 64-row steps on 2 x 8192 x 32 heads,
+// 8 x 2048 x 16 and 4 x 4096 x 16).  Grouped heads keep four pairs: a grouped
+// workgroup walks G query heads, so its grid is G times coarser, and 192-key
+// workgroups left a ragged last round (2 x 8192 tokens, 32 heads over 8
+// key/value heads: 13% slower).  At D = 64 one workgroup of eight pairs was
+// 8-18% slower than two of four.
+template <int D, bool SC = false, bool GROUPED = false>
 struct DkdvCfg {
   static constexpr bool WIDE = D >= 192;
   static constexpr bool SHORT = D == 64 || (D == 96 && !SC);  // 32-row tiles, two workgroups per CU
+  static constexpr bool SIX = D == 128 && !GROUPED;  // 32-row tiles, six pairs, three waves per SIMD
   static constexpr int WGS = SHORT ? 2 : 1;  // workgroups per CU
-  static constexpr int NPAIR = D == 256 ? 2 : 4;
-  static constexpr int NT = 128 * NPAIR;  // 8 waves (4 at D = 256)
+  static constexpr int NPAIR = D == 256 ? 2 : SIX ? 6 : 4;
+  static constexpr int NT = 128 * NPAIR;  // 8 waves (12 at D = 128, 4 at D = 256)
   static constexpr int BKV = 32 * NPAIR;  // keys per workgroup
-  static constexpr int BQ = (WIDE || SHORT) ? 32 : 64;  // query rows per streamed tile
+  static constexpr int BQ = (WIDE || SHORT || SIX) ? 32 : 64;  // query rows per streamed tile
   static constexpr int QB = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -315,9 +326,11 @@ struct DkdvCfg {
 // P-wave recomputes P from the capped scores and publishes
 // P (1 - tanh^2), so that the dS-wave's dS carries the cap's derivative).
 template <int D, bool GROUPED, bool SC>
-__global__ __launch_bounds__((DkdvCfg<D, SC>::NT), (DkdvCfg<D, SC>::WGS)) void bwd_dkdv_kernel(AttnArgs a, int ktiles) {
-  using C = DkdvCfg<D, SC>;
-  static_assert(C::NT == DkdvCfg<D>::NT && C::BKV == DkdvCfg<D>::BKV, "one grid for both instances");
+__global__ __launch_bounds__((DkdvCfg<D, SC, GROUPED>::NT), (DkdvCfg<D, SC, GROUPED>::WGS)) void bwd_dkdv_kernel(
+    AttnArgs a, int ktiles) {
+  using C = DkdvCfg<D, SC, GROUPED>;
+  static_assert(C::NT == DkdvCfg<D, false, GROUPED>::NT && C::BKV == DkdvCfg<D, false, GROUPED>::BKV,
+                "one grid with and without the cap");
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::NBUF * C::BUF];
   __shared__ __attribute__((aligned(16))) float fsm[C::NBUF * C::FBUF];
@@ -433,9 +446,10 @@ __global__ __launch_bounds__((DkdvCfg<D, SC>::NT), (DkdvCfg<D, SC>::WGS)) void b
   // barrier per step, nsteps + 1 steps.  In step j the P-wave computes S, P
   // and dV for tile j (products, elementwise, products); the dS-wave first
   // finishes tile j - 1 (dS from the dP it computed in the previous step,
-  // then dK) and then computes dP for tile j.  The two waves of a pair share
-  // a SIMD, and this order puts one wave's elementwise work beside the
-  // other's products.
+  // then dK) and then computes dP for tile j.  Waves go to the SIMDs in turn,
+  // so with four pairs the two waves of a pair (w and w + 4) share a SIMD,
+  // and this order puts one wave's elementwise work beside the other's
+  // products; with six, a SIMD holds three waves of different pairs.
   auto walk = [&](auto rolec) __attribute__((always_inline)) {
     constexpr bool PW = decltype(rolec)::value;
     // Per-lane LDS offsets (elements from the start of a buffer), fixed for
@@ -1038,6 +1052,18 @@ __global__ __launch_bounds__(DqCfg<D>::NT, (D < 192 ? 2 : 1)) void bwd_dq_kernel
   }
 }
 
+template <int D, bool GROUPED>
+static void launch_dkdv(const AttnArgs& a, bool diag, hipStream_t s) {
+  using KC = DkdvCfg<D, false, GROUPED>;
+  const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
+  const long long kblocks = (long long)ktiles * (diag ? 1 : a.nhalves) * a.B * a.Hkv * a.S;
+  const dim3 grid((unsigned)kblocks), block(KC::NT);
+  if (a.softcap > 0.f)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, GROUPED, true>), grid, block, 0, s, a, ktiles);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, GROUPED, false>), grid, block, 0, s, a, ktiles);
+}
+
 template <int D>
 static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
   if (stage == 0) {
@@ -1049,24 +1075,13 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
     else
       hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)qblocks), dim3(QC::NT), 0, s, a, qtiles);
   } else {
-    using KC = DkdvCfg<D>;
-    const int ktiles = (a.n + KC::BKV - 1) / KC::BKV;
     // with the noisy-diagonal kernel the main grid holds the clean key tiles
     // only (they come first in its order)
     const bool diag = use_noisy_diag(a.mode, a.b);
-    const long long kblocks = (long long)ktiles * (diag ? 1 : a.nhalves) * a.B * a.Hkv * a.S;
-    const dim3 grid((unsigned)kblocks), block(KC::NT);
-    if (a.softcap > 0.f) {
-      if (a.G > 1)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), grid, block, 0, s, a, ktiles);
-      else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), grid, block, 0, s, a, ktiles);
-    } else {
-      if (a.G > 1)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), grid, block, 0, s, a, ktiles);
-      else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), grid, block, 0, s, a, ktiles);
-    }
+    if (a.G > 1)
+      launch_dkdv<D, true>(a, diag, s);
+    else
+      launch_dkdv<D, false>(a, diag, s);
     if (a.S > 1) {
       const long long E = a.tokens * a.Hkv * D;
       const long long rblocks = (2 * E / 8 + 255) / 256;
@@ -1102,15 +1117,24 @@ static hipError_t launch_stage_t(const AttnArgs& a, int stage, hipStream_t s) {
 // the cap.
 constexpr long long kDkdvMinBlocksPerSlot = 4 * 256;
 
+template <int D>
+constexpr long long dkdv_min_blocks() {
+  return kDkdvMinBlocksPerSlot * DkdvCfg<D, false, true>::WGS;
+}
+
+// Only grouped heads split (G = 1 gives S = 1), so the grouped tile sizes
+// decide.
 int dkdv_group_splits(int B, int n, int nhalves, int Hkv, int G, int D) {
-  static_assert(DkdvCfg<64>::BKV == DkdvCfg<128>::BKV && DkdvCfg<96>::BKV == DkdvCfg<128>::BKV &&
-                    DkdvCfg<192>::BKV == DkdvCfg<128>::BKV,
-                "one key tile size below D = 256");
-  static_assert(DkdvCfg<96>::WGS == DkdvCfg<64>::WGS && DkdvCfg<192>::WGS == DkdvCfg<128>::WGS &&
-                    DkdvCfg<256>::WGS == DkdvCfg<128>::WGS,
-                "one occupancy for D <= 96, one above");
-  const int bkv = D == 256 ? DkdvCfg<256>::BKV : DkdvCfg<128>::BKV;
-  const long long min_blocks = kDkdvMinBlocksPerSlot * (D <= 96 ? DkdvCfg<64>::WGS : DkdvCfg<128>::WGS);
+  const int bkv = D == 64    ? DkdvCfg<64, false, true>::BKV
+                  : D == 96  ? DkdvCfg<96, false, true>::BKV
+                  : D == 128 ? DkdvCfg<128, false, true>::BKV
+                  : D == 192 ? DkdvCfg<192, false, true>::BKV
+                             : DkdvCfg<256, false, true>::BKV;
+  const long long min_blocks = D == 64    ? dkdv_min_blocks<64>()
+                               : D == 96  ? dkdv_min_blocks<96>()
+                               : D == 128 ? dkdv_min_blocks<128>()
+                               : D == 192 ? dkdv_min_blocks<192>()
+                                          : dkdv_min_blocks<256>();
   const long long ktiles = ((long long)n + bkv - 1) / bkv;
   const long long base = ktiles * nhalves * B * Hkv;
   int S = 1;
