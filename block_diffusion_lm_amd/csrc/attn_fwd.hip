@@ -62,10 +62,11 @@ __device__ __forceinline__ int half_offset(const AttnArgs& a, int half, int n) {
 // maximum, and kept in base-2 units).
 template <int D, int BN, int NW, int NBUF, bool SC>
 // D = 128: 32-key K / V tiles (32 KiB of LDS) and at most 168 registers,
-// three workgroups per CU.  D = 192 and 256: 32-key tiles, two workgroups
-// per CU (Q and O take most of half a register file).  D = 64: at most 128
-// registers, four workgroups per CU.
-__global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : (D == 128 && BN == 32) ? 3 : (NW == 4 && (D < 192 || BN == 32) ? 2 : 1))) void fwd_kernel(AttnArgs a, int qtiles) {
+// three workgroups per CU.  D = 96: 64-key tiles (48 KiB) and at most 168
+// registers, three workgroups per CU.  D = 192 and 256: 32-key tiles, two
+// workgroups per CU (Q and O take most of half a register file).  D = 64: at
+// most 128 registers, four workgroups per CU.
+__global__ __launch_bounds__(64 * NW, (D == 64 ? 4 : ((D == 128 && BN == 32) || (D == 96 && NW == 4)) ? 3 : (NW == 4 && (D < 192 || BN == 32) ? 2 : 1))) void fwd_kernel(AttnArgs a, int qtiles) {
   using C = FwdCfg<D, BN, NW, NBUF>;
   using Tile = typename C::Tile;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * C::BUF];
