@@ -7,7 +7,9 @@ the objects are linked into ``block_diffusion_lm_amd/libbdattn.so``.
 from __future__ import annotations
 
 import concurrent.futures
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -47,15 +49,51 @@ def hipcc() -> str:
 # Per-source code-generation options.
 SOURCE_FLAGS = {}
 
+# The compiler's per-kernel resource report (registers, scratch, occupancy)
+# of the last default build, for the checks in tests/test_kernel_resources.py.
+RESOURCES = os.path.join(ROOT, "_build", "kernel_resources.json")
 
-def _compile(src: str, extra) -> str:
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                     r"LDS Size \[bytes/block\]|VGPRs Spill|SGPRs Spill):\s+(\S+)")
+_FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+           "Occupancy [waves/SIMD]": "waves_per_simd", "LDS Size [bytes/block]": "lds",
+           "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill"}
+
+
+def kernel_key(mangled: str) -> str:
+    """``bd::<name><args>`` from a mangled kernel symbol, e.g.
+    ``fwd_kernel<128,32,4,2,0>`` (integer and bool template arguments)."""
+    m = re.match(r"_ZN2bd(\d+)", mangled)
+    if not m:
+        return mangled
+    i = m.end()
+    name = mangled[i:i + int(m.group(1))]
+    rest = mangled[i + int(m.group(1)):]
+    args = re.findall(r"L[ib](-?\d+)E", rest) if rest.startswith("I") else []
+    return f"{name}<{','.join(args)}>" if args else name
+
+
+def parse_resources(text: str) -> dict:
+    """Per kernel, the fields of the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        field, value = m.group(1), m.group(2)
+        if field == "Function Name":
+            cur = out.setdefault(kernel_key(value), {})
+        elif cur is not None:
+            cur[_FIELDS[field]] = int(value)
+    return out
+
+
+def _compile(src: str, extra) -> tuple:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     extra = list(SOURCE_FLAGS.get(src, [])) + list(extra)
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + list(extra)
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + list(extra) +
+           ["-Rpass-analysis=kernel-resource-usage"])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, parse_resources(r.stderr)
 
 
 def build(extra_flags=(), verbose: bool = True, out: str = None, source_flags=None) -> str:
@@ -73,8 +111,16 @@ def build(extra_flags=(), verbose: bool = True, out: str = None, source_flags=No
         BUILD_DIR = os.path.join(ROOT, "_build", os.path.basename(out) + ".d")
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
     BUILD_DIR = saved_dir
+    objs = [obj for obj, _ in results]
+    if not out and not extra_flags and source_flags is None:
+        resources = {}
+        for _, res in results:
+            resources.update(res)
+        os.makedirs(os.path.dirname(RESOURCES), exist_ok=True)
+        with open(RESOURCES, "w") as f:
+            json.dump(resources, f, indent=1, sort_keys=True)
     tmp = lib_path + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
