@@ -413,7 +413,7 @@ def test_largest_workload_sampled():
 
 
 # Every (sample, head) of the full-size workloads, on a fixed set of positions.
-EVERY_HEAD = ["c2", "c3", "c4"] + C5
+EVERY_HEAD = ["c2", "c3", "c4"] + C5 + ["h1", "h2", "h3", "g1", "g2", "g3"]
 
 
 def head_positions(n, b, j, seed):
@@ -467,23 +467,33 @@ def kv_columns(n, b, pos, window):
 def _workload_result(name):
     """Inputs and GPU outputs of a full-size workload, launched as the
     benchmark launches it (kept for the consecutive parts of one workload)."""
-    w = WORKLOADS[name]
+    w = {**WORKLOADS, **HEAD_DIM_WORKLOADS, **GQA_WORKLOADS}[name]
     q, k, v, do = make_workload_inputs(w)
     scale = 1 / math.sqrt(w.D)
-    return w, (q, k, v, do), run_diffusion(q, k, v, do, w.b, scale)
+    run = run_grouped if w.kv_heads != w.H else run_diffusion
+    return w, (q, k, v, do), run(q, k, v, do, w.b, scale)
 
 
-def _head_refs(qh, kh, vh, dh, n, b, D, scale, pos, window):
-    """Oracle values one (sample, head) is checked against (see
-    test_every_head_sampled)."""
+def _q_refs(qh, kh, vh, dh, n, b, scale, pos):
+    """O, LSE and dQ of one query head at the rows of ``pos`` in both halves
+    (see test_every_head_sampled)."""
     rows = np.array(pos + [n + p for p in pos], dtype=np.int64)
     O, L = oracle.diffusion_forward_rows(qh, kh, vh, b, scale, rows)
     dq_ref = oracle.diffusion_grad_q_rows(qh, kh, vh, dh, b, scale, rows)
-    cols, seen = kv_columns(n, b, pos, window)
-    Of, Lf = np.zeros((2 * n, D)), np.zeros(2 * n)
-    Of[seen], Lf[seen] = oracle.diffusion_forward_rows(qh, kh, vh, b, scale, seen)
-    dk_ref, dv_ref = oracle.diffusion_grad_kv_cols(qh, kh, vh, dh, Of, Lf, b, scale, cols)
-    return rows, O, L, dq_ref, cols, dk_ref, dv_ref
+    return rows, O, L, dq_ref
+
+
+def _kv_refs(qhs, kh, vh, dhs, n, b, D, scale, cols, seen):
+    """dK and dV of one key/value head at the key columns ``cols``: the sum
+    over the query heads that read it (qhs, dhs), each needing O and LSE of
+    the rows ``seen`` that see those columns."""
+    dk_ref, dv_ref = 0.0, 0.0
+    for qh, dh in zip(qhs, dhs):
+        Of, Lf = np.zeros((2 * n, D)), np.zeros(2 * n)
+        Of[seen], Lf[seen] = oracle.diffusion_forward_rows(qh, kh, vh, b, scale, seen)
+        dk, dv = oracle.diffusion_grad_kv_cols(qh, kh, vh, dh, Of, Lf, b, scale, cols)
+        dk_ref, dv_ref = dk_ref + dk, dv_ref + dv
+    return dk_ref, dv_ref
 
 
 def _full_row_stats(qh, kh, vh, b, scale, ex, chunk=2048):
@@ -498,39 +508,58 @@ def _full_row_stats(qh, kh, vh, b, scale, ex, chunk=2048):
 @pytest.mark.parametrize("name", EVERY_HEAD)
 def test_every_head_sampled(name):
     """Every (sample, head) of the full-size workloads, as the benchmark
-    launches them: O, LSE and dQ at the rows head_positions names (in both
-    halves), and dK / dV at the key columns kv_columns derives from them (the
-    clean columns within the last max(512, 2^21 / 2n) positions of the half,
-    all of it at c2).  The gradients are held to 2e-2 times the largest
-    oracle value of their tensor that this test computes: every sampled row
-    and column of every head, plus the first 64 clean key columns of head
-    (0, 0) (seen by nearly every row, they carry the largest dK and dV), a
-    lower bound of the tensor's maximum.  The oracle runs on one thread per
-    (sample, head) (one BLAS thread each)."""
+    launches them: O, LSE and dQ of every query head at the rows
+    head_positions names (in both halves, j = sample * H + head), and dK / dV
+    of every key/value head at the key columns kv_columns derives from
+    head_positions for j = sample * H_kv + kv head (the clean columns within
+    the last max(512, 2^21 / 2n) positions of the half, all of it at c2);
+    with grouped heads the reference dK / dV sums over the query heads of the
+    group.  The gradients are held to 2e-2 times the largest oracle value of
+    their tensor that this test computes: every sampled row and column of
+    every head, plus the first 64 clean key columns of key/value head (0, 0)
+    (seen by nearly every row, they carry the largest dK and dV), a lower
+    bound of the tensor's maximum.  The oracle runs on one thread per task
+    (one BLAS thread each)."""
     import concurrent.futures
     from threadpoolctl import threadpool_limits
     w, (q, k, v, do), res = _workload_result(name)
     scale = 1 / math.sqrt(w.D)
-    n, b = w.n, w.b
+    n, b, H, Hkv = w.n, w.b, w.H, w.kv_heads
+    G = H // Hkv
     window = min(n, max(512, 2 ** 21 // (2 * n)))
     f = lambda x: oracle.to_f64(x)
-    pairs = [divmod(j, w.H) for j in range(w.B * w.H)]
+    qpairs = [divmod(j, H) for j in range(w.B * H)]
+    kvpairs = [divmod(j, Hkv) for j in range(w.B * Hkv)]
+    kvcols = {bh: kv_columns(n, b, head_positions(n, b, bh[0] * Hkv + bh[1], w.seed), window) for bh in kvpairs}
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        refs = list(ex.map(lambda bh: _head_refs(*(f(x[bh[0], :, bh[1]]) for x in (q, k, v, do)), n, b, w.D, scale,
-                                                 head_positions(n, b, bh[0] * w.H + bh[1], w.seed), window),
-                           pairs))
-        q0, k0, v0, d0 = (f(x[0, :, 0]) for x in (q, k, v, do))
-        O0, L0 = _full_row_stats(q0, k0, v0, b, scale, ex)
-    early = n + np.arange(min(64, n))
-    dk0, dv0 = oracle.diffusion_grad_kv_cols(q0, k0, v0, d0, O0, L0, b, scale, early)
-    gmax = {"dq": max(np.abs(r[3]).max() for r in refs),
-            "dk": max(max(np.abs(r[5]).max() for r in refs), np.abs(dk0).max()),
-            "dv": max(max(np.abs(r[6]).max() for r in refs), np.abs(dv0).max())}
+        qrefs = list(ex.map(lambda bh: _q_refs(f(q[bh[0], :, bh[1]]), f(k[bh[0], :, bh[1] // G]),
+                                               f(v[bh[0], :, bh[1] // G]), f(do[bh[0], :, bh[1]]), n, b, scale,
+                                               head_positions(n, b, bh[0] * H + bh[1], w.seed)),
+                            qpairs))
+        kvrefs = list(ex.map(lambda bh: _kv_refs([f(q[bh[0], :, bh[1] * G + g]) for g in range(G)],
+                                                 f(k[bh[0], :, bh[1]]), f(v[bh[0], :, bh[1]]),
+                                                 [f(do[bh[0], :, bh[1] * G + g]) for g in range(G)],
+                                                 n, b, w.D, scale, *kvcols[bh]),
+                             kvpairs))
+        k0, v0 = f(k[0, :, 0]), f(v[0, :, 0])
+        early = n + np.arange(min(64, n))
+        dk0, dv0 = 0.0, 0.0
+        for g in range(G):
+            q0, d0 = f(q[0, :, g]), f(do[0, :, g])
+            O0, L0 = _full_row_stats(q0, k0, v0, b, scale, ex)
+            dk, dv = oracle.diffusion_grad_kv_cols(q0, k0, v0, d0, O0, L0, b, scale, early)
+            dk0, dv0 = dk0 + dk, dv0 + dv
+    gmax = {"dq": max(np.abs(r[3]).max() for r in qrefs),
+            "dk": max(max(np.abs(r[0]).max() for r in kvrefs), np.abs(dk0).max()),
+            "dv": max(max(np.abs(r[1]).max() for r in kvrefs), np.abs(dv0).max())}
     checks = [(0, 0, "dk", early, dk0), (0, 0, "dv", early, dv0)]
-    for (bi, hi), (rows, O, L, dq_ref, cols, dk_ref, dv_ref) in zip(pairs, refs):
+    for (bi, hi), (rows, O, L, dq_ref) in zip(qpairs, qrefs):
         check_fwd(res["out"][bi, rows, hi], res["lse"][bi, hi, rows], O, L, f"{name} ({bi},{hi})", name)
-        checks += [(bi, hi, "dq", rows, dq_ref), (bi, hi, "dk", cols, dk_ref), (bi, hi, "dv", cols, dv_ref)]
+        checks.append((bi, hi, "dq", rows, dq_ref))
+    for (bi, hk), (dk_ref, dv_ref) in zip(kvpairs, kvrefs):
+        cols = kvcols[(bi, hk)][0]
+        checks += [(bi, hk, "dk", cols, dk_ref), (bi, hk, "dv", cols, dv_ref)]
     for bi, hi, gname, idx, ref in checks:
         check_grad_scaled(res[gname][bi, idx, hi], ref, gmax[gname], gname, f"{name} ({bi},{hi})", name)
 
@@ -850,6 +879,67 @@ def test_varlen_workloads(name):
         check_grad(res["dq"][None, s0:s1, hs], dQ, "dq", tag, name)
         check_grad(res["dk"][None, s0:s1, j:j + 1], dK, "dk", tag, name)
         check_grad(res["dv"][None, s0:s1, j:j + 1], dV, "dv", tag, name)
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_WORKLOADS))
+def test_varlen_every_head_sampled(name):
+    """Every (sample, head) of the packed workloads, as the benchmark
+    launches them, on the positions test_every_head_sampled uses (per sample,
+    with its own half length): O, LSE and dQ of every query head, dK and dV
+    of every key/value head (summed over its group).  Gradients are held to
+    2e-2 times the largest oracle value computed (the first 64 clean key
+    columns of the longest sample's first key/value head included)."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    w = VARLEN_WORKLOADS[name]
+    q, k, v, do, cu = make_varlen_workload_inputs(w)
+    ns = w.half_lengths
+    scale = 1 / math.sqrt(w.D)
+    res = run_varlen(q, k, v, do, cu, max(ns), w.b, scale)
+    f = oracle.to_f64
+    H, Hkv, b = w.H, w.kv_heads, w.b
+    G = H // Hkv
+    samples = [bi for bi in range(len(ns)) if ns[bi] > 0]
+    win = lambda n: min(n, max(512, 2 ** 21 // (2 * n)))
+    qtasks = [(bi, hh) for bi in samples for hh in range(H)]
+    kvtasks = [(bi, hk) for bi in samples for hk in range(Hkv)]
+    kvcols = {(bi, hk): kv_columns(ns[bi], b, head_positions(ns[bi], b, bi * Hkv + hk, w.seed), win(ns[bi]))
+              for bi, hk in kvtasks}
+    sl = lambda x, bi, h: f(x[cu[bi]:cu[bi + 1], h])
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        qrefs = list(ex.map(lambda t: _q_refs(sl(q, t[0], t[1]), sl(k, t[0], t[1] // G), sl(v, t[0], t[1] // G),
+                                              sl(do, t[0], t[1]), ns[t[0]], b, scale,
+                                              head_positions(ns[t[0]], b, t[0] * H + t[1], w.seed)),
+                            qtasks))
+        kvrefs = list(ex.map(lambda t: _kv_refs([sl(q, t[0], t[1] * G + g) for g in range(G)],
+                                                sl(k, t[0], t[1]), sl(v, t[0], t[1]),
+                                                [sl(do, t[0], t[1] * G + g) for g in range(G)],
+                                                ns[t[0]], b, w.D, scale, *kvcols[t]),
+                             kvtasks))
+        bl = max(samples, key=lambda i: ns[i])
+        nl = ns[bl]
+        early = nl + np.arange(min(64, nl))
+        k0, v0 = sl(k, bl, 0), sl(v, bl, 0)
+        dk0, dv0 = 0.0, 0.0
+        for g in range(G):
+            q0, d0 = sl(q, bl, g), sl(do, bl, g)
+            O0, L0 = _full_row_stats(q0, k0, v0, b, scale, ex)
+            dk, dv = oracle.diffusion_grad_kv_cols(q0, k0, v0, d0, O0, L0, b, scale, early)
+            dk0, dv0 = dk0 + dk, dv0 + dv
+    gmax = {"dq": max(np.abs(r[3]).max() for r in qrefs),
+            "dk": max(max(np.abs(r[0]).max() for r in kvrefs), np.abs(dk0).max()),
+            "dv": max(max(np.abs(r[1]).max() for r in kvrefs), np.abs(dv0).max())}
+    checks = [(bl, 0, "dk", early, dk0), (bl, 0, "dv", early, dv0)]
+    for (bi, hh), (rows, O, L, dq_ref) in zip(qtasks, qrefs):
+        tok = cu[bi] + rows
+        check_fwd(res["out"][tok, hh], res["lse"][hh, tok], O, L, f"{name} sample {bi} head {hh}", name)
+        checks.append((bi, hh, "dq", rows, dq_ref))
+    for (bi, hk), (dk_ref, dv_ref) in zip(kvtasks, kvrefs):
+        cols = kvcols[(bi, hk)][0]
+        checks += [(bi, hk, "dk", cols, dk_ref), (bi, hk, "dv", cols, dv_ref)]
+    for bi, h, gname, idx, ref in checks:
+        check_grad_scaled(res[gname][cu[bi] + idx, h], ref, gmax[gname], gname, f"{name} sample {bi} head {h}", name)
 
 
 def test_varlen_autograd_wrapper():
