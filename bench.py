@@ -605,11 +605,12 @@ def main():
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
                 "algorithmic_flops_per_launch": per_kernel_flops[dom],
                 "avg_launch_ms": kern_avg[dom]}
-    # MFMA-busy share and clock of each kernel from the committed counter
+    # MFMA- and vector-busy shares and clock of each kernel from the committed counter
     # runs, while the kernel sources are the ones they were taken on
     ctr = profiling.read_counters(os.path.join(args.profiles, f"counters_{w.name}.txt"))
     if ctr and ctr.get("source_sha256") == profiling.source_hash():
         roofline["mfma_busy"] = {k: v.get("mfma_busy") for k, v in ctr.items() if isinstance(v, dict)}
+        roofline["valu_busy"] = {k: v.get("valu_busy") for k, v in ctr.items() if isinstance(v, dict)}
         roofline["counter_clock_mhz"] = {k: v.get("clock_mhz") for k, v in ctr.items() if isinstance(v, dict)}
 
     # ---- interleaved rounds against the causal yardstick --------------------

@@ -181,6 +181,8 @@ COUNTER_PASSES = [
      "SQ_WAIT_INST_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"],
     ["FETCH_SIZE"],
     ["WRITE_SIZE"],
+    ["GRBM_GUI_ACTIVE", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC",
+     "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32"],
 ]
 NUM_CU = 256      # MI355X compute units
 SIMD_PER_CU = 4
@@ -214,6 +216,8 @@ def counters_summary(workload: str, trace: str, pmc_dbs, commands, copy_mib: int
               "#   clock_mhz = GRBM_GUI_ACTIVE / 8 XCDs / duration",
               "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 256 CU * 4 SIMD):",
               "#     the share of the matrix cores' cycles spent on MFMAs (32 cycles per 32x32x16 bf16)",
+              "#   valu_busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / 8 XCDs * 256 CU): the share of",
+              "#     the vector units' issue cycles in use (quad-cycles per CU, rocprofv3's VALUBusy)",
               "#   mfma_tflops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 flop / duration",
               "#   valu_per_mfma, lds_per_mfma, salu_per_mfma = instruction counts / SQ_INSTS_MFMA",
               "#   hbm_gbs = (FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale) KiB / duration,",
@@ -233,6 +237,8 @@ def counters_summary(workload: str, trace: str, pmc_dbs, commands, copy_mib: int
         if v.get("SQ_VALU_MFMA_BUSY_CYCLES") and v.get("GRBM_GUI_ACTIVE"):
             cyc = v["GRBM_GUI_ACTIVE"] / NUM_XCD * NUM_CU * SIMD_PER_CU
             lines.append(f"  {'mfma_busy':32s} {v['SQ_VALU_MFMA_BUSY_CYCLES'] / cyc:.4f}")
+        if v.get("SQ_ACTIVE_INST_VALU") and v.get("GRBM_GUI_ACTIVE"):
+            lines.append(f"  {'valu_busy':32s} {v['SQ_ACTIVE_INST_VALU'] / (v['GRBM_GUI_ACTIVE'] / NUM_XCD * NUM_CU):.4f}")
         if v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16") and dur:
             lines.append(f"  {'mfma_tflops':32s} {v['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / (dur * 1e-9) / 1e12:.1f}")
         if mf:

@@ -116,12 +116,12 @@ def test_roofline_at_the_sampled_clock():
 
 
 def test_committed_counters_parse():
-    """profiles/counters_c4.txt: every kernel has an MFMA-busy share in (0, 1]
-    and a clock; the file names the sources it was taken on."""
+    """profiles/counters_c4.txt: every kernel has MFMA- and vector-busy
+    shares in (0, 1] and a clock; the file names the sources it was taken on."""
     c = profiling.read_counters(os.path.join(ROOT, "profiles", "counters_c4.txt"))
     assert c is not None and len(c["source_sha256"]) == 64
     kernels = {k: v for k, v in c.items() if isinstance(v, dict)}
     assert set(kernels) == {"fwd", "bwd_dq", "bwd_dkdv"}
     for v in kernels.values():
-        assert 0 < v["mfma_busy"] <= 1 and 1000 < v["clock_mhz"] < 2600
+        assert 0 < v["mfma_busy"] <= 1 and 0 < v["valu_busy"] <= 1 and 1000 < v["clock_mhz"] < 2600
         assert v["SQ_LDS_BANK_CONFLICT"] >= 0 and v["hbm_gbs"] > 0
