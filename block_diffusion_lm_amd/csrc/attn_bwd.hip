@@ -5,8 +5,9 @@
 //          stores -delta and lse2 (float32) in the caller's workspace; then
 //          it walks the key tiles its rows see and accumulates
 //          dQ = scale * dS K;
-//   dkdv : one workgroup per 128-key tile of one key/value head (runs
-//          after dq, reading the workspace); it walks the query tiles that
+//   dkdv : one workgroup per key tile of one key/value head (192 keys for
+//          multi-head D = 128, 64 at D = 256, 128 otherwise; runs after dq,
+//          reading the workspace); it walks the query tiles that
 //          see its keys, for every query head that reads the key/value head
 //          in turn, and accumulates dV = P^T dO and dK = scale * dS^T Q in
 //          registers.  With grouped query heads the key tile is loaded once
@@ -22,8 +23,8 @@
 // sees.  Neither kernel uses atomics, so the result is deterministic.
 //
 // Mapping to gfx950 (MFMA layouts in common.h, LDS tiles in tile_io.h):
-//  dkdv: each wave owns 32 keys and holds K and V as B operands in
-//    registers for the whole walk.  S = Q K^T and dP = dO V^T come out with
+//  dkdv: each pair of waves owns 32 keys, one holding K and the other V as
+//    B operands in registers for the whole walk.  S = Q K^T and dP = dO V^T come out with
 //    one key per lane and the query rows in registers; read with k = query
 //    row they are directly the B operands of dV^T += dO^T P and
 //    dK^T += Q^T dS, whose A operands come from the natural Q and dO tiles
